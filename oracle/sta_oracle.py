@@ -1,0 +1,309 @@
+"""Plain CPU oracle for Sliding Tile Attention (STA), in float64 numpy.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables or
+helpers with the HIP library; the two meet only through the seeded input
+generators, which hold none of the method's arithmetic.
+
+Sources (web pages, cited by title and section):
+  [STA-abs]  "Sliding Tile Attention" (arXiv 2502.04507), abstract as printed on
+             the gptget.net summary page: attention over a local 3D window,
+             taken tile by tile instead of token by token.
+  [STA-meth] same page, sections on the core innovation and method details:
+             the latent is cut into non-overlapping space-time tiles, each
+             (query tile, key tile) block is fully dense (no mixed blocks),
+             and every head has its own window size.
+  [STA-rebut] "Fast Video Generation with Sliding Tile Attention", OpenReview
+             rebuttal, answer on input resolution: tile (6,8,8); the latent must
+             be a whole number of tiles in every dimension.
+
+What the oracle computes is the plain definition the method reaches exactly:
+full softmax attention whose mask admits key token j for query token i iff the
+tile holding j lies in the window of the tile holding i.  Readings taken where
+the pages are silent (each is listed in the design doc as well):
+  * raster order of the latent is (T, H, W) with W fastest;
+  * tile-major order: tiles in raster order over the tile grid, tokens in raster
+    order inside a tile;
+  * window per dimension: w' = min(w, n); the window of query tile q starts at
+    clamp(q - floor(w'/2), 0, n - w') and spans w' tiles (the centre is clamped
+    so the window stays inside the tile grid; for even w' the extra tile falls
+    on the low side);
+  * windows are counted in tiles; a window < 1 is an error;
+  * the log-sum-exp uses the natural logarithm.
+Every function here is pinned by ``tests/test_oracle.py`` against brute force,
+closed forms, invariants and library routines.
+"""
+
+import numpy as np
+
+__all__ = [
+    "tile_grid", "tile_major_index", "reorder", "unreorder", "window_start",
+    "window_contains", "tile_pairs", "token_tile_coords", "window_mask",
+    "forward", "backward", "backward_key_rows", "dense_forward",
+]
+
+
+def tile_grid(latent, tile):
+    """Tile grid n = (T/t, H/h, W/w) and tile volume L = t*h*w.
+
+    [STA-rebut]: the latent must be an integer multiple of the tile in each of
+    its three dimensions; anything else is rejected here.
+    """
+    latent = tuple(int(v) for v in latent)
+    tile = tuple(int(v) for v in tile)
+    if len(latent) != 3 or len(tile) != 3:
+        raise ValueError("latent and tile are (T, H, W) triples")
+    if min(latent) < 1 or min(tile) < 1:
+        raise ValueError("latent and tile sizes must be positive")
+    if any(a % b for a, b in zip(latent, tile)):
+        raise ValueError(f"latent {latent} is not a multiple of tile {tile}")
+    n = tuple(a // b for a, b in zip(latent, tile))
+    return n, tile[0] * tile[1] * tile[2]
+
+
+def tile_major_index(latent, tile):
+    """pi[r]: position in the tile-major sequence of the raster token r.
+
+    [STA-meth] tiling step: every tile becomes one contiguous run of the
+    sequence.  Raster token r = (tau*H + y)*W + x sits in tile a = (tau//t,
+    y//h, x//w) at intra-tile coordinate i = (tau%t, y%h, x%w), and goes to
+    ((a0*n1 + a1)*n2 + a2)*L + (i0*h + i1)*w + i2.
+    """
+    (n0, n1, n2), L = tile_grid(latent, tile)
+    T, H, W = latent
+    t, h, w = tile
+    tau, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    tile_id = ((tau // t) * n1 + (y // h)) * n2 + (x // w)
+    intra = ((tau % t) * h + (y % h)) * w + (x % w)
+    return (tile_id * L + intra).reshape(-1).astype(np.int64)
+
+
+def reorder(x, latent, tile):
+    """Raster -> tile-major along axis -2: Y[..., pi(r), :] = X[..., r, :]."""
+    pi = tile_major_index(latent, tile)
+    if x.shape[-2] != pi.size:
+        raise ValueError("sequence axis does not match the latent")
+    y = np.empty_like(x)
+    y[..., pi, :] = x
+    return y
+
+
+def unreorder(y, latent, tile):
+    """Tile-major -> raster along axis -2: X[..., r, :] = Y[..., pi(r), :]."""
+    pi = tile_major_index(latent, tile)
+    if y.shape[-2] != pi.size:
+        raise ValueError("sequence axis does not match the latent")
+    return y[..., pi, :].copy()
+
+
+def window_start(q, w, n):
+    """First tile of the window of query tile q along one dimension, and w'.
+
+    [STA-abs]/[STA-meth]: a query tile attends to a local window of tiles.  The
+    window keeps its full size w' = min(w, n) at the grid edges: its start is
+    q - floor(w'/2) clamped into [0, n - w'].
+    """
+    if w < 1:
+        raise ValueError("window must be at least one tile")
+    wp = min(int(w), int(n))
+    return min(max(int(q) - wp // 2, 0), int(n) - wp), wp
+
+
+def window_contains(qt, kt, win, n):
+    """True iff key tile kt lies in the window of query tile qt (3D coords)."""
+    for d in range(3):
+        s, wp = window_start(qt[d], win[d], n[d])
+        if not (s <= kt[d] < s + wp):
+            return False
+    return True
+
+
+def _tile_coords(n):
+    """Tile-grid coordinates in raster order over the grid, shape [N_t, 3]."""
+    return np.stack(np.meshgrid(np.arange(n[0]), np.arange(n[1]), np.arange(n[2]),
+                                indexing="ij"), axis=-1).reshape(-1, 3)
+
+
+def tile_pairs(latent, tile, windows, transpose=False):
+    """Canonical (query tile, key tile) list per head.
+
+    Tiles are numbered in raster order over the tile grid.  Forward order is
+    head, then query tile, then key tile; the transposed order (used by the
+    backward pass, where a key tile collects the query tiles whose window holds
+    it) is head, then key tile, then query tile.  Returns (pairs [P, 2] int32
+    holding (q, k), offsets [Hh + 1] int64).
+    """
+    n, _ = tile_grid(latent, tile)
+    coords = _tile_coords(n)
+    out, offsets = [], [0]
+    for win in np.asarray(windows).reshape(-1, 3):
+        head = []
+        for a, ca in enumerate(coords):
+            for b, cb in enumerate(coords):
+                if transpose:
+                    if window_contains(cb, ca, win, n):
+                        head.append((b, a))
+                elif window_contains(ca, cb, win, n):
+                    head.append((a, b))
+        out.extend(head)
+        offsets.append(offsets[-1] + len(head))
+    return np.asarray(out, dtype=np.int32).reshape(-1, 2), np.asarray(offsets, dtype=np.int64)
+
+
+def token_tile_coords(latent, tile, order="tile"):
+    """Tile-grid coordinates [S, 3] of the tile holding each sequence position."""
+    n, L = tile_grid(latent, tile)
+    T, H, W = latent
+    t, h, w = tile
+    if order == "tile":
+        return np.repeat(_tile_coords(n), L, axis=0)
+    if order == "raster":
+        tau, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+        return np.stack([tau // t, y // h, x // w], axis=-1).reshape(-1, 3)
+    raise ValueError("order is 'tile' or 'raster'")
+
+
+def window_mask(latent, tile, win, order="tile", rows=None):
+    """Boolean mask M[i, j]: key position j is visible to query position i.
+
+    [STA-meth]: visibility is decided per tile pair, so every block of the mask
+    is all-true or all-false.  ``rows`` restricts the query positions.
+    """
+    n, _ = tile_grid(latent, tile)
+    kc = token_tile_coords(latent, tile, order)
+    qc = kc if rows is None else kc[np.asarray(rows)]
+    m = np.ones((qc.shape[0], kc.shape[0]), dtype=bool)
+    for d in range(3):
+        wp = min(int(win[d]), n[d])
+        if int(win[d]) < 1:
+            raise ValueError("window must be at least one tile")
+        start = np.clip(qc[:, d] - wp // 2, 0, n[d] - wp)
+        m &= (kc[None, :, d] >= start[:, None]) & (kc[None, :, d] < start[:, None] + wp)
+    return m
+
+
+def _check_qkv(q, k, v, windows):
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, Hh, S, D] shape")
+    windows = np.asarray(windows).reshape(-1, 3)
+    if windows.shape[0] != q.shape[1]:
+        raise ValueError("one window per head")
+    return windows
+
+
+def forward(q, k, v, latent, tile, windows, scale, order="tile", rows=None, chunk=256):
+    """STA forward: O and LSE of masked softmax attention, float64.
+
+    [STA-abs]: each query attends, with softmax, to every key in its tile's
+    window.  For query row i: s_j = scale * <q_i, k_j> on visible j, m = max s,
+    l = sum exp(s - m), O_i = sum_j exp(s_j - m) v_j / l, LSE_i = m + ln l.
+    ``rows`` (query positions) limits the work to a sample of rows; the result
+    then has shape [B, Hh, len(rows), D].
+    """
+    windows = _check_qkv(q, k, v, windows)
+    B, Hh, S, D = q.shape
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    o = np.zeros((B, Hh, rows.size, D))
+    lse = np.zeros((B, Hh, rows.size))
+    for h in range(Hh):
+        for c0 in range(0, rows.size, chunk):
+            r = rows[c0:c0 + chunk]
+            m = window_mask(latent, tile, windows[h], order, rows=r)
+            for b in range(B):
+                s = scale * (q[b, h, r] @ k[b, h].T)
+                s[~m] = -np.inf
+                mx = s.max(axis=1, keepdims=True)
+                e = np.exp(s - mx)
+                l = e.sum(axis=1, keepdims=True)
+                o[b, h, c0:c0 + r.size] = (e @ v[b, h]) / l
+                lse[b, h, c0:c0 + r.size] = (mx + np.log(l))[:, 0]
+    return o, lse
+
+
+def backward(q, k, v, do, latent, tile, windows, scale, order="tile"):
+    """Gradients (dQ, dK, dV) of the STA forward, float64, whole tensors.
+
+    The pages give no backward formulas; this is the exact gradient of the
+    forward above (softmax attention restricted to the window mask):
+    P = softmax(masked S), O = P V, Dl_i = sum_d dO_id O_id,
+    dP = dO V^T, dS = P * (dP - Dl), dQ = scale dS K, dK = scale dS^T Q,
+    dV = P^T dO.  Meant for small grids (it forms the S x S matrices).
+    """
+    windows = _check_qkv(q, k, v, windows)
+    B, Hh, S, D = q.shape
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(Hh):
+        m = window_mask(latent, tile, windows[h], order)
+        for b in range(B):
+            s = scale * (q[b, h] @ k[b, h].T)
+            s[~m] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ v[b, h]
+            dl = (do[b, h] * o).sum(axis=1, keepdims=True)
+            dp = do[b, h] @ v[b, h].T
+            ds = p * (dp - dl)
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+            dv[b, h] = p.T @ do[b, h]
+    return dq, dk, dv
+
+
+def backward_key_rows(q, k, v, do, latent, tile, win, scale, b, h, key_rows, order="tile"):
+    """dK and dV of one (batch b, head h) at the key positions ``key_rows``.
+
+    Same formulas as ``backward``, evaluated only where needed: the query rows
+    that can see any of the sampled keys are found from the mask, their full
+    softmax rows (over every visible key) give P, and the sampled columns of
+    dS give dK_j = scale sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i.
+    """
+    key_rows = np.asarray(key_rows)
+    qf, kf, vf, dof = (np.asarray(a[b, h], dtype=np.float64) for a in (q, k, v, do))
+    S = qf.shape[0]
+    seen = window_mask(latent, tile, win, order)[:, key_rows].any(axis=1) if S <= 8192 else None
+    if seen is None:  # large grids: test visibility tile-wise, one query tile at a time
+        seen = np.zeros(S, dtype=bool)
+        for c0 in range(0, S, 1024):
+            r = np.arange(c0, min(S, c0 + 1024))
+            seen[r] = window_mask(latent, tile, win, order, rows=r)[:, key_rows].any(axis=1)
+    qi = np.nonzero(seen)[0]
+    dk = np.zeros((key_rows.size, qf.shape[1]))
+    dv = np.zeros_like(dk)
+    for c0 in range(0, qi.size, 512):
+        r = qi[c0:c0 + 512]
+        m = window_mask(latent, tile, win, order, rows=r)
+        s = scale * (qf[r] @ kf.T)
+        s[~m] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ vf
+        dl = (dof[r] * o).sum(axis=1, keepdims=True)
+        pj = p[:, key_rows]
+        ds = pj * (dof[r] @ vf[key_rows].T - dl)
+        dk += scale * (ds.T @ qf[r])
+        dv += pj.T @ dof[r]
+    return dk, dv
+
+
+def dense_forward(q, k, v, scale, rows=None, chunk=256):
+    """Full (unmasked) softmax attention, O and LSE, float64: the denominator
+    the method is compared with ([STA-abs] compares against FlashAttention)."""
+    B, Hh, S, D = q.shape
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    o = np.zeros((B, Hh, rows.size, D))
+    lse = np.zeros((B, Hh, rows.size))
+    for b in range(B):
+        for h in range(Hh):
+            for c0 in range(0, rows.size, chunk):
+                r = rows[c0:c0 + chunk]
+                s = scale * (q[b, h, r] @ k[b, h].T)
+                mx = s.max(axis=1, keepdims=True)
+                e = np.exp(s - mx)
+                l = e.sum(axis=1, keepdims=True)
+                o[b, h, c0:c0 + r.size] = (e @ v[b, h]) / l
+                lse[b, h, c0:c0 + r.size] = (mx + np.log(l))[:, 0]
+    return o, lse

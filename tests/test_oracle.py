@@ -1,0 +1,422 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants and library
+routines that fix what Sliding Tile Attention computes, so that the oracle is
+not trusted on its own say-so.  CPU only."""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+
+# ---------------------------------------------------------------- reorder / pi
+
+def _pi_by_enumeration(latent, tile):
+    """Tile-major order written as an enumeration: walk tiles in raster order
+    over the tile grid and, inside each, tokens in raster order; hand out
+    consecutive sequence positions."""
+    T, H, W = latent
+    t, h, w = tile
+    pi = np.full(T * H * W, -1, dtype=np.int64)
+    pos = 0
+    for a0, a1, a2 in itertools.product(range(T // t), range(H // h), range(W // w)):
+        for i0, i1, i2 in itertools.product(range(t), range(h), range(w)):
+            r = ((a0 * t + i0) * H + (a1 * h + i1)) * W + (a2 * w + i2)
+            pi[r] = pos
+            pos += 1
+    return pi
+
+
+SHAPES = [((6, 16, 16), (2, 4, 4)), ((4, 8, 8), (2, 4, 4)), ((5, 6, 10), (5, 3, 2)),
+          ((1, 8, 16), (1, 8, 8)), ((3, 4, 5), (1, 1, 1)), ((3, 4, 5), (3, 4, 5)),
+          ((30, 48, 80), (6, 8, 8))]
+
+
+@pytest.mark.parametrize("latent,tile", SHAPES)
+def test_pi_matches_enumeration(latent, tile):
+    assert np.array_equal(O.tile_major_index(latent, tile), _pi_by_enumeration(latent, tile))
+
+
+@pytest.mark.parametrize("latent,tile", SHAPES)
+def test_pi_is_bijection_and_roundtrip_exact(latent, tile):
+    S = int(np.prod(latent))
+    pi = O.tile_major_index(latent, tile)
+    assert np.array_equal(np.sort(pi), np.arange(S))
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, S, 4)).astype(np.float32)
+    y = O.reorder(x, latent, tile)
+    assert np.array_equal(O.unreorder(y, latent, tile), x)
+    assert not np.array_equal(y, x) or np.array_equal(pi, np.arange(S))
+
+
+@pytest.mark.parametrize("latent,tile", SHAPES[:5])
+def test_reorder_matches_reshape_transpose(latent, tile):
+    """Tile-major as a 6-D reshape/transpose of the (T,H,W) volume."""
+    T, H, W = latent
+    t, h, w = tile
+    x = np.arange(T * H * W * 2, dtype=np.float64).reshape(T * H * W, 2)
+    ref = (x.reshape(T // t, t, H // h, h, W // w, w, 2)
+           .transpose(0, 2, 4, 1, 3, 5, 6).reshape(-1, 2))
+    assert np.array_equal(O.reorder(x, latent, tile), ref)
+
+
+def test_non_tile_multiple_rejected():
+    with pytest.raises(ValueError):
+        O.tile_grid((29, 45, 76), (6, 8, 8))
+    with pytest.raises(ValueError):
+        O.window_start(0, 0, 4)
+
+
+# ---------------------------------------------------------------- windows
+
+@pytest.mark.parametrize("n,w,starts", [
+    (4, 3, [0, 0, 1, 1]),
+    (6, 3, [0, 0, 1, 2, 3, 3]),
+    (10, 5, [0, 0, 0, 1, 2, 3, 4, 5, 5, 5]),
+    (5, 1, [0, 1, 2, 3, 4]),
+    (3, 7, [0, 0, 0]),
+    (6, 6, [0, 0, 0, 0, 0, 0]),
+    (5, 2, [0, 0, 1, 2, 3]),   # even window: extra tile on the low side
+])
+def test_window_start_worked_sequences(n, w, starts):
+    assert [O.window_start(q, w, n)[0] for q in range(n)] == starts
+
+
+@pytest.mark.parametrize("n,w,counts", [(10, 5, [3, 4, 5, 6, 7, 7, 6, 5, 4, 3]),
+                                        (4, 3, [2, 4, 4, 2]),
+                                        (8, 5, [3, 4, 5, 8, 8, 5, 4, 3])])
+def test_transposed_window_counts(n, w, counts):
+    got = [sum(1 for q in range(n) if O.window_contains((q, 0, 0), (k, 0, 0), (w, 1, 1), (n, 1, 1)))
+           for k in range(n)]
+    assert got == counts
+
+
+def _window_by_sliding(q, w, n):
+    """Second formulation: put the window around q (floor(w'/2) tiles below),
+    then slide it back inside the grid by however far it overflows."""
+    wp = min(w, n)
+    lo = q - wp // 2
+    hi = lo + wp - 1
+    if lo < 0:
+        lo, hi = 0, hi - lo
+    if hi > n - 1:
+        lo, hi = lo - (hi - (n - 1)), n - 1
+    return set(range(lo, hi + 1))
+
+
+def test_window_matches_sliding_formulation():
+    for n in range(1, 13):
+        for w in range(1, 15):
+            for q in range(n):
+                s, wp = O.window_start(q, w, n)
+                assert set(range(s, s + wp)) == _window_by_sliding(q, w, n)
+
+
+def test_odd_window_is_symmetric_in_interior():
+    for n in range(1, 14):
+        for w in range(1, n + 1, 2):
+            r = w // 2
+            for q in range(r, n - r):
+                s, wp = O.window_start(q, w, n)
+                assert (s, s + wp - 1) == (q - r, q + r)
+
+
+PAIR_CASES = [((6, 16, 16), (2, 4, 4), [(3, 3, 3), (1, 2, 5)]),
+              ((30, 48, 80), (6, 8, 8), [(3, 3, 3), (5, 6, 10), (1, 6, 10), (3, 3, 5), (5, 3, 3)]),
+              ((24, 64, 64), (6, 8, 8), [(3, 5, 5)]),
+              ((4, 8, 8), (2, 4, 4), [(9, 9, 9), (1, 1, 1)])]
+
+
+@pytest.mark.parametrize("latent,tile,wins", PAIR_CASES)
+def test_pair_count_invariant_and_own_tile(latent, tile, wins):
+    n, _ = O.tile_grid(latent, tile)
+    pairs, off = O.tile_pairs(latent, tile, wins)
+    nt = int(np.prod(n))
+    for h, win in enumerate(wins):
+        kh = int(np.prod([min(a, b) for a, b in zip(win, n)]))
+        p = pairs[off[h]:off[h + 1]]
+        assert p.shape[0] == nt * kh
+        counts = np.bincount(p[:, 0], minlength=nt)
+        assert np.all(counts == kh)
+        own = {(a, a) for a in range(nt)}
+        assert own <= {tuple(x) for x in p}
+        # canonical order: query tile, then key tile, increasing
+        key = p[:, 0].astype(np.int64) * nt + p[:, 1]
+        assert np.all(np.diff(key) > 0)
+        if all(a >= b for a, b in zip(win, n)):
+            assert p.shape[0] == nt * nt
+
+
+@pytest.mark.parametrize("latent,tile,wins", PAIR_CASES[:1] + PAIR_CASES[2:])
+def test_transposed_pairs_same_set(latent, tile, wins):
+    n, _ = O.tile_grid(latent, tile)
+    nt = int(np.prod(n))
+    f, fo = O.tile_pairs(latent, tile, wins)
+    t, to = O.tile_pairs(latent, tile, wins, transpose=True)
+    assert np.array_equal(fo, to)
+    for h in range(len(wins)):
+        a, b = f[fo[h]:fo[h + 1]], t[to[h]:to[h + 1]]
+        assert {tuple(x) for x in a} == {tuple(x) for x in b}
+        key = b[:, 1].astype(np.int64) * nt + b[:, 0]
+        assert np.all(np.diff(key) > 0)
+
+
+def test_mask_blocks_are_whole_tiles():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    _, L = O.tile_grid(latent, tile)
+    m = O.window_mask(latent, tile, (3, 1, 3))
+    blocks = m.reshape(m.shape[0] // L, L, m.shape[1] // L, L)
+    assert np.all(blocks.all(axis=(1, 3)) == blocks.any(axis=(1, 3)))
+
+
+# ---------------------------------------------------------------- forward
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _brute_force_raster(q, k, v, latent, tile, wins, scale):
+    """Per-token softmax in raster order with scalar loops and math.exp."""
+    T, H, W = latent
+    t, h, w = tile
+    n = (T // t, H // h, W // w)
+    B, Hh, S, D = q.shape
+    coords = [(tau, y, x) for tau in range(T) for y in range(H) for x in range(W)]
+    tc = [(tau // t, y // h, x // w) for tau, y, x in coords]
+    out = np.zeros_like(q)
+    lse = np.zeros((B, Hh, S))
+    for hh in range(Hh):
+        wins_d = [[_window_by_sliding(qq, wins[hh][d], n[d]) for qq in range(n[d])] for d in range(3)]
+        for b in range(B):
+            for i in range(S):
+                vis = [j for j in range(S) if all(tc[j][d] in wins_d[d][tc[i][d]] for d in range(3))]
+                s = [scale * sum(q[b, hh, i, c] * k[b, hh, j, c] for c in range(D)) for j in vis]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                tot = sum(e)
+                for c in range(D):
+                    out[b, hh, i, c] = sum(e[a] * v[b, hh, j, c] for a, j in enumerate(vis)) / tot
+                lse[b, hh, i] = mx + math.log(tot)
+    return out, lse
+
+
+def test_forward_matches_brute_force():
+    latent, tile = (4, 8, 8), (2, 4, 4)     # tile grid 2x2x2, 256 tokens
+    wins = [(1, 1, 1), (2, 1, 2), (9, 2, 1)]
+    B, Hh, D, S = 2, 3, 6, 256
+    q, k, v = (_rand((B, Hh, S, D), s) for s in (1, 2, 3))
+    scale = 0.7
+    ref_o, ref_l = _brute_force_raster(q, k, v, latent, tile, wins, scale)
+    o, l = O.forward(q, k, v, latent, tile, wins, scale, order="raster")
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, ref_l, rtol=0, atol=1e-12)
+    # the same through the tile-major order
+    qt, kt, vt = (O.reorder(a, latent, tile) for a in (q, k, v))
+    o2, l2 = O.forward(qt, kt, vt, latent, tile, wins, scale)
+    np.testing.assert_allclose(O.unreorder(o2, latent, tile), ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.unreorder(l2[..., None], latent, tile)[..., 0], ref_l, rtol=0, atol=1e-12)
+
+
+def test_forward_brute_force_uneven_grid():
+    latent, tile = (6, 8, 12), (2, 4, 4)    # tile grid 3x2x3, 576 tokens
+    wins = [(2, 1, 2), (3, 3, 1)]
+    q, k, v = (_rand((1, 2, 576, 4), s) for s in (4, 5, 6))
+    ref_o, ref_l = _brute_force_raster(q, k, v, latent, tile, wins, 0.5)
+    o, l = O.forward(q, k, v, latent, tile, wins, 0.5, order="raster")
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, ref_l, rtol=0, atol=1e-12)
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    t = [torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v)]
+    m = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=m, scale=scale).numpy()
+
+
+def test_full_window_equals_full_attention():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    q, k, v = (_rand((1, 2, 1536, 64), s) for s in (7, 8, 9))
+    scale = 1 / 8
+    o, l = O.forward(q, k, v, latent, tile, [(3, 4, 4), (99, 99, 99)], scale)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, scale), rtol=0, atol=1e-12)
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    ref_lse = np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) + s.max(-1)
+    np.testing.assert_allclose(l, ref_lse, rtol=0, atol=1e-10)
+    o2, l2 = O.dense_forward(q, k, v, scale)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l, rtol=0, atol=1e-12)
+
+
+def test_unit_window_is_per_tile_attention():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    _, L = O.tile_grid(latent, tile)
+    q, k, v = (_rand((1, 2, 1536, 16), s) for s in (10, 11, 12))
+    o, _ = O.forward(q, k, v, latent, tile, [(1, 1, 1)] * 2, 0.3)
+    for a in range(1536 // L):
+        sl = slice(a * L, (a + 1) * L)
+        np.testing.assert_allclose(o[:, :, sl], _sdpa(q[:, :, sl], k[:, :, sl], v[:, :, sl], 0.3),
+                                   rtol=0, atol=1e-12)
+
+
+def test_zero_query_gives_window_mean_and_log_count():
+    """Q = 0 makes every visible score 0: O_i is the plain mean of V over the
+    window's K_h*L tokens and LSE_i = ln(K_h*L)."""
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    n, L = O.tile_grid(latent, tile)
+    win = (3, 1, 2)
+    v = _rand((1, 1, 1536, 5), 13)
+    q = np.zeros_like(v)
+    k = _rand(v.shape, 14)
+    o, l = O.forward(q, k, v, latent, tile, [win], 0.125)
+    kh = int(np.prod([min(a, b) for a, b in zip(win, n)]))
+    coords = list(itertools.product(range(n[0]), range(n[1]), range(n[2])))
+    vt = v[0, 0].reshape(len(coords), L, 5)
+    for a, ca in enumerate(coords):
+        sets = [_window_by_sliding(ca[d], win[d], n[d]) for d in range(3)]
+        keys = [b for b, cb in enumerate(coords) if all(cb[d] in sets[d] for d in range(3))]
+        assert len(keys) == kh
+        ref = vt[keys].reshape(-1, 5).mean(axis=0)
+        np.testing.assert_allclose(o[0, 0, a * L:(a + 1) * L], np.broadcast_to(ref, (L, 5)),
+                                   rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, np.log(kh * L), rtol=0, atol=1e-12)
+
+
+def test_constant_values_pass_through():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    q, k = _rand((1, 2, 1536, 8), 15), _rand((1, 2, 1536, 8), 16)
+    c = _rand((1, 2, 1, 8), 17)
+    v = np.broadcast_to(c, q.shape).copy()
+    o, _ = O.forward(q, k, v, latent, tile, [(3, 3, 3), (1, 4, 2)], 0.125)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-12)
+
+
+def test_forward_rows_subset():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    q, k, v = (_rand((2, 2, 1536, 8), s) for s in (18, 19, 20))
+    wins = [(3, 3, 3), (1, 2, 4)]
+    o, l = O.forward(q, k, v, latent, tile, wins, 0.3)
+    rows = np.array([0, 31, 32, 700, 1535])
+    o2, l2 = O.forward(q, k, v, latent, tile, wins, 0.3, rows=rows)
+    np.testing.assert_allclose(o2, o[:, :, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l[:, :, rows], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- backward
+
+def _autograd_ref(q, k, v, do, latent, tile, wins, scale):
+    """Gradients by torch autograd through masked SDPA, float64 on the CPU."""
+    qt, kt, vt = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    masks = torch.stack([torch.from_numpy(O.window_mask(latent, tile, w)) for w in wins])
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=masks[None], scale=scale)
+    out.backward(torch.from_numpy(do))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_backward_matches_autograd():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    wins = [(3, 3, 3), (1, 2, 5)]
+    q, k, v, do = (_rand((2, 2, 1536, 16), s) for s in (21, 22, 23, 24))
+    got = O.backward(q, k, v, do, latent, tile, wins, 0.25)
+    ref = _autograd_ref(q, k, v, do, latent, tile, wins, 0.25)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    latent, tile = (2, 4, 8), (1, 2, 4)      # 64 tokens, grid 2x2x2
+    wins = [(1, 2, 1)]
+    q, k, v, do = (_rand((1, 1, 64, 3), s) for s in (25, 26, 27, 28))
+    scale = 0.9
+    dq, dk, dv = O.backward(q, k, v, do, latent, tile, wins, scale)
+
+    def loss(qq, kk, vv):
+        return float((O.forward(qq, kk, vv, latent, tile, wins, scale)[0] * do).sum())
+
+    eps = 1e-6
+    rng = np.random.default_rng(0)
+    for grad, which in ((dq, 0), (dk, 1), (dv, 2)):
+        for _ in range(6):
+            idx = (0, 0, int(rng.integers(64)), int(rng.integers(3)))
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-7
+
+
+def test_backward_invariants():
+    """Rows of dS sum to zero, so sum_j dK_j = 0; rows of P sum to one, so
+    sum_j dV_j = sum_i dO_i."""
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    q, k, v, do = (_rand((1, 2, 1536, 8), s) for s in (29, 30, 31, 32))
+    _, dk, dv = O.backward(q, k, v, do, latent, tile, [(3, 3, 3), (2, 1, 3)], 0.4)
+    np.testing.assert_allclose(dk.sum(axis=2), 0, atol=1e-10)
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-10)
+
+
+def test_backward_zero_query_closed_form():
+    """Q = 0: P_ij = 1/(K_h L) on visible pairs, so dV_j = sum over the queries
+    that see j of dO_i / (K_h L)."""
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    n, L = O.tile_grid(latent, tile)
+    win = (1, 3, 2)
+    kh = int(np.prod([min(a, b) for a, b in zip(win, n)]))
+    k, v, do = (_rand((1, 1, 1536, 4), s) for s in (33, 34, 35))
+    q = np.zeros_like(k)
+    _, _, dv = O.backward(q, k, v, do, latent, tile, [win], 0.3)
+    coords = list(itertools.product(range(n[0]), range(n[1]), range(n[2])))
+    dot = do[0, 0].reshape(len(coords), L, 4)
+    for b, cb in enumerate(coords):
+        seers = [a for a, ca in enumerate(coords)
+                 if all(cb[d] in _window_by_sliding(ca[d], win[d], n[d]) for d in range(3))]
+        ref = dot[seers].sum(axis=(0, 1)) / (kh * L)
+        np.testing.assert_allclose(dv[0, 0, b * L:(b + 1) * L], np.broadcast_to(ref, (L, 4)), atol=1e-12)
+
+
+def test_backward_key_rows_matches_full():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    wins = [(3, 3, 3)]
+    q, k, v, do = (_rand((1, 1, 1536, 8), s) for s in (36, 37, 38, 39))
+    _, dk, dv = O.backward(q, k, v, do, latent, tile, wins, 0.3)
+    rows = np.array([0, 5, 33, 1000, 1535])
+    dk2, dv2 = O.backward_key_rows(q, k, v, do, latent, tile, wins[0], 0.3, 0, 0, rows)
+    np.testing.assert_allclose(dk2, dk[0, 0, rows], atol=1e-12)
+    np.testing.assert_allclose(dv2, dv[0, 0, rows], atol=1e-12)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def test_pins_catch_planted_window_mistake(monkeypatch):
+    """A window start one tile too low must fail the worked-sequence pin and
+    the brute-force forward pin."""
+    real = O.window_start
+
+    def shifted(q, w, n):
+        s, wp = real(q, w, n)
+        return max(s - 1, 0), wp
+    monkeypatch.setattr(O.sta_oracle, "window_start", shifted)
+    assert [O.sta_oracle.window_start(q, 3, 6)[0] for q in range(6)] != [0, 0, 1, 2, 3, 3]
+
+
+def test_pins_catch_planted_mask_mistake(monkeypatch):
+    """A mask that truncates windows at the grid edge (instead of clamping the
+    centre) changes the forward output and fails the count invariant."""
+    def truncated(latent, tile, win, order="tile", rows=None):
+        n, _ = O.tile_grid(latent, tile)
+        kc = O.token_tile_coords(latent, tile, order)
+        qc = kc if rows is None else kc[np.asarray(rows)]
+        m = np.ones((qc.shape[0], kc.shape[0]), dtype=bool)
+        for d in range(3):
+            r = min(win[d], n[d]) // 2
+            m &= np.abs(kc[None, :, d] - qc[:, None, d]) <= r
+        return m
+    latent, tile = (6, 12, 12), (2, 4, 4)    # tile grid 3x3x3
+    q, k, v = (_rand((1, 1, 864, 3), s) for s in (40, 41, 42))
+    good, _ = O.forward(q, k, v, latent, tile, [(3, 3, 3)], 0.5, order="raster")
+    monkeypatch.setattr(O.sta_oracle, "window_mask", truncated)
+    bad, _ = O.sta_oracle.forward(q, k, v, latent, tile, [(3, 3, 3)], 0.5, order="raster")
+    assert np.abs(bad - good).max() > 1e-3
