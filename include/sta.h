@@ -1,0 +1,144 @@
+/*
+ * libsta: Sliding Tile Attention (STA) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are web pages, cited by title and section):
+ *   [STA-abs]   "Sliding Tile Attention" (arXiv 2502.04507), abstract as printed
+ *               on the gptget.net summary page: softmax attention where every
+ *               query attends only to keys inside a local 3D (T,H,W) window, the
+ *               window being taken tile by tile instead of token by token.
+ *   [STA-meth]  same page, sections on the core innovation and method details:
+ *               the latent is cut into non-overlapping space-time tiles made
+ *               contiguous in the sequence; every (query tile, key tile) block is
+ *               either fully computed or skipped, never half masked; every head
+ *               has its own window size.
+ *   [STA-rebut] "Fast Video Generation with Sliding Tile Attention", OpenReview
+ *               rebuttal, answer on input resolution: tile (6,8,8); the latent
+ *               must be an integer multiple of the tile.
+ *
+ * Conventions shared by every entry point
+ *   - Shapes are (T, H, W) triples, W fastest.  A raster token r = (tau*H+y)*W+x.
+ *   - Tensors are contiguous [B, Hh, S, D] (D innermost), S = T*H*W, element type
+ *     bf16 (STA_BF16) or fp32 (STA_F32, the fp32 debug instance).  LSE is fp32
+ *     [B, Hh, S] in the same token order as the tensors it belongs to.
+ *   - Tile-major order: tiles in raster order over the tile grid
+ *     n = (T/t, H/h, W/w), tokens in raster order inside a tile; tile number a
+ *     occupies sequence positions [a*L, (a+1)*L), L = t*h*w.
+ *   - Window of a head: (wt, wh, ww) in tiles, each >= 1.  Along a dimension with
+ *     n tiles, w' = min(w, n) and the window of query tile q covers tiles
+ *     [s, s + w') with s = clamp(q - floor(w'/2), 0, n - w'): the centre is
+ *     clamped so the window always stays inside the tile grid and always holds
+ *     w' tiles.  The window table is a HOST array int32 [Hh][3], read during the
+ *     call only (the caller may free it on return); at most STA_MAX_HEADS heads.
+ *   - All tensor pointers are device memory owned by the caller, 16-byte aligned.
+ *     The library never allocates device memory.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Kernel
+ *     launches are asynchronous: a return of STA_OK means the work was queued.
+ *   - Return value: STA_OK (0) or a negative STA_ERR_* code.  Every argument is
+ *     validated before anything is launched; on an error nothing is launched and
+ *     no output is touched.  There is no mutable global state: calls are
+ *     thread-safe; calls that write the same buffers must be ordered by the caller.
+ */
+#ifndef STA_H_
+#define STA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t t, h, w;
+} sta_dim3;
+
+typedef enum { STA_BF16 = 0, STA_F32 = 1 } sta_dtype;
+
+enum {
+  STA_OK = 0,
+  STA_ERR_ARG = -1,               /* null pointer, non-positive size, bad scale */
+  STA_ERR_NOT_TILE_MULTIPLE = -2, /* latent not a whole number of tiles [STA-rebut] */
+  STA_ERR_WINDOW = -3,            /* a window entry < 1 */
+  STA_ERR_UNSUPPORTED = -4,       /* head_dim, tile volume or dtype not built */
+  STA_ERR_ALIGN = -5,             /* a tensor pointer not 16-byte aligned */
+  STA_ERR_HIP = -6,               /* the HIP runtime reported an error at launch */
+  STA_ERR_WORKSPACE = -7,         /* workspace missing or smaller than required */
+  STA_ERR_TOO_LARGE = -8          /* a size exceeds the kernels' 32-bit index range */
+};
+
+#define STA_MAX_HEADS 256
+
+/* Human-readable text for a return code (static storage). */
+const char* sta_strerror(int code);
+
+/* Tile reorder [STA-meth], raster -> tile-major along S:
+ *   y[b, hh, pi(r), :] = x[b, hh, r, :]
+ * where pi(r) is the tile-major position of raster token r.  x and y are
+ * distinct [B, Hh, S, D] buffers of type dt.  A bit-exact copy. */
+int sta_tile_reorder(const void* x, void* y, int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
+                     sta_dim3 tile, sta_dtype dt, void* stream);
+
+/* Inverse of sta_tile_reorder: x[b, hh, r, :] = y[b, hh, pi(r), :]. */
+int sta_tile_unreorder(const void* y, void* x, int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
+                       sta_dim3 tile, sta_dtype dt, void* stream);
+
+/* Number of (query tile, key tile) pairs over all heads: sum_h N_t * prod_d w'_d
+ * ([STA-meth]: the blocks that are computed).  The transposed list has the same
+ * count.  Host only; returns a negative STA_ERR_* code on bad arguments. */
+int64_t sta_tile_pairs_count(sta_dim3 latent, sta_dim3 tile, const int32_t* win_host, int64_t Hh);
+
+/* Canonical tile-pair list, written by a kernel that uses the same window
+ * function as sta_forward / sta_backward.  Tiles are numbered in raster order
+ * over the tile grid.  pairs_dev: device int32 [count][2] of (q_tile, k_tile).
+ * transpose = 0: ordered by head, then query tile, then key tile (the forward's
+ * view); transpose = 1: by head, then key tile, then query tile (the set of query
+ * tiles whose window holds a key tile: the backward's view).  head_offsets_host
+ * (nullable): host int64 [Hh + 1], prefix offsets of each head's pairs, filled
+ * before return. */
+int sta_tile_pairs(int32_t* pairs_dev, int64_t* head_offsets_host, sta_dim3 latent, sta_dim3 tile,
+                   const int32_t* win_host, int64_t Hh, int transpose, void* stream);
+
+/* Same list computed on the host into host memory (pairs_host int32 [count][2]),
+ * with the same window function compiled for the CPU. */
+int sta_tile_pairs_host(int32_t* pairs_host, int64_t* head_offsets_host, sta_dim3 latent,
+                        sta_dim3 tile, const int32_t* win_host, int64_t Hh, int transpose);
+
+/* STA forward [STA-abs]: for every (b, hh) and query position i of query tile a,
+ *   O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j   over key positions j whose
+ *   tile lies in the window of a,   LSE_i = ln sum_j exp(scale * <q_i, k_j>).
+ * q, k, v, o: [B, Hh, S, D] in TILE-MAJOR order (see sta_tile_reorder).
+ * lse: fp32 [B, Hh, S] or NULL.  scale > 0 (usually 1/sqrt(D)).
+ * STA_BF16: bf16 in/out, fp32 accumulation, MFMA; needs D in {64, 128} and
+ * L % 32 == 0.  STA_F32: fp32 in/out, fp32 arithmetic; needs D <= 128. */
+int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
+                float scale, sta_dtype dt, void* stream);
+
+/* Bytes of device workspace sta_backward needs (0 is a valid answer). */
+size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dtype dt);
+
+/* STA backward: the exact gradient of sta_forward (the pages name fine-tuning
+ * with STA [STA-meth], which needs it).  With P the window-masked softmax,
+ *   Dl_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Dl_i),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+ *   dV_j = sum_i P_ij dO_i.
+ * Inputs q, k, v, o, dout (tile-major, type dt) and lse (fp32, from
+ * sta_forward); outputs dq, dk, dv (tile-major, type dt), fully overwritten.
+ * workspace: device memory of at least sta_backward_workspace_bytes(), owned by
+ * the caller, contents on entry irrelevant. */
+int sta_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                 int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                 const int32_t* win_host, float scale, sta_dtype dt, void* stream);
+
+/* Dense softmax attention over all S keys: the full-attention baseline STA is
+ * compared with ([STA-abs] compares with FlashAttention).  Same kernel family
+ * and layout as sta_forward; S % 64 == 0 for STA_BF16. */
+int sta_dense_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t Hh, int64_t S, int64_t D, float scale, sta_dtype dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STA_H_ */

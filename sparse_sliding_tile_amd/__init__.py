@@ -1,0 +1,7 @@
+"""Sliding Tile Attention for AMD MI355X: a thin Python face over libsta.so.
+
+The library is loaded on first use; without it every call raises.
+"""
+from ._lib import (STA_BF16, STA_F32, StaError, backward, backward_workspace_bytes,  # noqa: F401
+                   dense_forward, forward, lib, strerror, tile_pairs, tile_pairs_count,
+                   tile_pairs_host, tile_reorder, tile_unreorder)

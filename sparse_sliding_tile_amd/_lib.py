@@ -1,0 +1,213 @@
+"""ctypes binding of libsta (include/sta.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libsta.so.  torch supplies device memory and the current stream.
+There is no fallback: without the built library every call raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsta.so")
+
+STA_BF16 = 0
+STA_F32 = 1
+STA_MAX_HEADS = 256
+
+c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Dim3(ctypes.Structure):
+    _fields_ = [("t", c_i32), ("h", c_i32), ("w", c_i32)]
+
+
+# name -> (restype, argtypes); mirrors include/sta.h
+SIGNATURES = {
+    "sta_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "sta_tile_reorder": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int, c_vp]),
+    "sta_tile_unreorder": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int, c_vp]),
+    "sta_tile_pairs_count": (c_i64, [Dim3, Dim3, c_vp, c_i64]),
+    "sta_tile_pairs": (ctypes.c_int, [c_vp, c_vp, Dim3, Dim3, c_vp, c_i64, ctypes.c_int, c_vp]),
+    "sta_tile_pairs_host": (ctypes.c_int, [c_vp, c_vp, Dim3, Dim3, c_vp, c_i64, ctypes.c_int]),
+    "sta_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
+                                   c_f32, ctypes.c_int, c_vp]),
+    "sta_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, Dim3, ctypes.c_int]),
+    "sta_backward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                    c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
+    "sta_dense_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
+                                         c_f32, ctypes.c_int, c_vp]),
+}
+
+_lib = None
+
+
+class StaError(RuntimeError):
+    def __init__(self, code, fn):
+        self.code = code
+        super().__init__(f"{fn}: {strerror(code)} (code {code})")
+
+
+def lib():
+    """The loaded libsta.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_sliding_tile_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(code):
+    return lib().sta_strerror(int(code)).decode()
+
+
+def _check(code, fn):
+    if code != 0:
+        raise StaError(int(code), fn)
+
+
+def _dim3(x):
+    t, h, w = (int(a) for a in x)
+    return Dim3(t, h, w)
+
+
+def _windows(windows, heads):
+    arr = np.ascontiguousarray(np.asarray(windows, dtype=np.int32).reshape(-1, 3))
+    if arr.shape[0] == 1 and heads > 1:
+        arr = np.ascontiguousarray(np.repeat(arr, heads, axis=0))
+    if arr.shape[0] != heads:
+        raise ValueError(f"need one window per head ({heads}), got {arr.shape[0]}")
+    return arr
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return STA_BF16
+    if t.dtype == torch.float32:
+        return STA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape4(x, name):
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B, Hh, S, D]")
+    return x.shape
+
+
+def tile_reorder(x, latent, tile, out=None):
+    """Raster -> tile-major along S of a [B, Hh, S, D] tensor."""
+    B, Hh, S, D = _shape4(x, "x")
+    out = torch.empty_like(x) if out is None else out
+    _check(lib().sta_tile_reorder(_dev(x, "x"), _dev(out, "out"), B, Hh, D, _dim3(latent), _dim3(tile),
+                                  _dtype(x), _stream(x)), "sta_tile_reorder")
+    return out
+
+
+def tile_unreorder(y, latent, tile, out=None):
+    """Tile-major -> raster along S of a [B, Hh, S, D] tensor."""
+    B, Hh, S, D = _shape4(y, "y")
+    out = torch.empty_like(y) if out is None else out
+    _check(lib().sta_tile_unreorder(_dev(y, "y"), _dev(out, "out"), B, Hh, D, _dim3(latent), _dim3(tile),
+                                    _dtype(y), _stream(y)), "sta_tile_unreorder")
+    return out
+
+
+def tile_pairs_count(latent, tile, windows):
+    w = _windows(windows, len(np.asarray(windows).reshape(-1, 3)))
+    n = lib().sta_tile_pairs_count(_dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), w.shape[0])
+    if n < 0:
+        raise StaError(int(n), "sta_tile_pairs_count")
+    return int(n)
+
+
+def tile_pairs(latent, tile, windows, transpose=False, device="cuda"):
+    """Pair list computed on the GPU: (int32 [P, 2] tensor, int64 offsets [Hh+1])."""
+    w = _windows(windows, len(np.asarray(windows).reshape(-1, 3)))
+    n = tile_pairs_count(latent, tile, w)
+    out = torch.empty((max(n, 1), 2), dtype=torch.int32, device=device)
+    off = np.zeros(w.shape[0] + 1, dtype=np.int64)
+    _check(lib().sta_tile_pairs(_dev(out, "pairs"), off.ctypes.data_as(c_vp), _dim3(latent), _dim3(tile),
+                                w.ctypes.data_as(c_vp), w.shape[0], int(bool(transpose)), _stream(out)),
+           "sta_tile_pairs")
+    return out[:n], off
+
+
+def tile_pairs_host(latent, tile, windows, transpose=False):
+    """Same list computed by the library on the host: (int32 [P, 2], int64 [Hh+1])."""
+    w = _windows(windows, len(np.asarray(windows).reshape(-1, 3)))
+    n = tile_pairs_count(latent, tile, w)
+    out = np.zeros((max(n, 1), 2), dtype=np.int32)
+    off = np.zeros(w.shape[0] + 1, dtype=np.int64)
+    _check(lib().sta_tile_pairs_host(out.ctypes.data_as(c_vp), off.ctypes.data_as(c_vp), _dim3(latent),
+                                     _dim3(tile), w.ctypes.data_as(c_vp), w.shape[0], int(bool(transpose))),
+           "sta_tile_pairs_host")
+    return out[:n], off
+
+
+def forward(q, k, v, latent, tile, windows, scale=None, out=None, lse=None, want_lse=True):
+    """STA forward on tile-major [B, Hh, S, D] tensors: returns (O, LSE or None)."""
+    B, Hh, S, D = _shape4(q, "q")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    w = _windows(windows, Hh)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hh, S), dtype=torch.float32, device=q.device)
+    lp = _dev(lse, "lse") if lse is not None else c_vp(None)
+    _check(lib().sta_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, D,
+                             _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale, _dtype(q),
+                             _stream(q)), "sta_forward")
+    return out, lse
+
+
+def backward_workspace_bytes(B, Hh, D, latent, dtype=torch.bfloat16):
+    dt = STA_BF16 if dtype == torch.bfloat16 else STA_F32
+    return int(lib().sta_backward_workspace_bytes(B, Hh, D, _dim3(latent), dt))
+
+
+def backward(q, k, v, o, do, lse, latent, tile, windows, scale=None, workspace=None):
+    """STA backward on tile-major tensors: returns (dQ, dK, dV)."""
+    B, Hh, S, D = _shape4(q, "q")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    w = _windows(windows, Hh)
+    nbytes = backward_workspace_bytes(B, Hh, D, latent, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib().sta_backward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(do, "do"),
+                              _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"),
+                              _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                              B, Hh, D, _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale,
+                              _dtype(q), _stream(q)), "sta_backward")
+    return dq, dk, dv
+
+
+def dense_forward(q, k, v, scale=None, out=None, want_lse=True):
+    """Full softmax attention over all S keys: returns (O, LSE or None)."""
+    B, Hh, S, D = _shape4(q, "q")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hh, S), dtype=torch.float32, device=q.device) if want_lse else None
+    lp = _dev(lse, "lse") if lse is not None else c_vp(None)
+    _check(lib().sta_dense_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, S, D,
+                                   scale, _dtype(q), _stream(q)), "sta_dense_forward")
+    return out, lse

@@ -1,0 +1,273 @@
+// C-ABI of libsta: argument validation, per-launch tables, dispatch.
+//
+// Every check happens before the first launch, so an error return leaves the
+// outputs untouched.  Window tables are copied into the kernel arguments of the
+// launch that uses them; nothing is kept between calls.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace sta;
+
+namespace {
+
+int to_status(hipError_t e) { return e == hipSuccess ? STA_OK : STA_ERR_HIP; }
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+int make_geometry(sta_dim3 latent, sta_dim3 tile, Geometry* g) {
+  if (latent.t < 1 || latent.h < 1 || latent.w < 1 || tile.t < 1 || tile.h < 1 || tile.w < 1)
+    return STA_ERR_ARG;
+  if (latent.t % tile.t || latent.h % tile.h || latent.w % tile.w) return STA_ERR_NOT_TILE_MULTIPLE;
+  const int64_t S = (int64_t)latent.t * latent.h * latent.w;
+  if (S >= (1ll << 31)) return STA_ERR_TOO_LARGE;
+  g->T = latent.t;
+  g->H = latent.h;
+  g->W = latent.w;
+  g->t = tile.t;
+  g->h = tile.h;
+  g->w = tile.w;
+  g->n0 = latent.t / tile.t;
+  g->n1 = latent.h / tile.h;
+  g->n2 = latent.w / tile.w;
+  g->L = tile.t * tile.h * tile.w;
+  g->S = (int)S;
+  g->ntiles = g->n0 * g->n1 * g->n2;
+  return STA_OK;
+}
+
+// Clamps windows to the grid (w' = min(w, n)) and orders heads for launch:
+// heaviest window first (stable), then dealt round-robin over the 8 XCD slots
+// so that each XCD's contiguous run of work items gets a similar load.
+int make_heads(const int32_t* win, int64_t Hh, const Geometry& g, HeadTable* ht) {
+  if (win == nullptr || Hh < 1) return STA_ERR_ARG;
+  if (Hh > STA_MAX_HEADS) return STA_ERR_UNSUPPORTED;
+  memset(ht, 0, sizeof(*ht));
+  const int n[3] = {g.n0, g.n1, g.n2};
+  std::vector<int64_t> weight(Hh);
+  for (int64_t h = 0; h < Hh; ++h) {
+    weight[h] = 1;
+    for (int d = 0; d < 3; ++d) {
+      const int32_t w = win[3 * h + d];
+      if (w < 1) return STA_ERR_WINDOW;
+      ht->wp[h][d] = (uint16_t)window_width(w, n[d]);
+      weight[h] *= ht->wp[h][d];
+    }
+  }
+  std::vector<int> idx(Hh);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return weight[a] > weight[b]; });
+  int pos = 0;
+  for (int x = 0; x < 8; ++x)
+    for (int64_t j = x; j < Hh; j += 8) ht->order[pos++] = (uint8_t)idx[j];
+  return STA_OK;
+}
+
+int elem_bytes(sta_dtype dt) { return dt == STA_BF16 ? 2 : (dt == STA_F32 ? 4 : 0); }
+
+int check_sizes(int64_t B, int64_t Hh, int64_t D, const Geometry& g) {
+  if (B < 1 || Hh < 1 || D < 1) return STA_ERR_ARG;
+  if (B * Hh * (int64_t)g.ntiles >= (1ll << 31) / 4) return STA_ERR_TOO_LARGE;
+  return STA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sta_strerror(int code) {
+  switch (code) {
+    case STA_OK: return "success";
+    case STA_ERR_ARG: return "invalid argument (null pointer, non-positive size or scale)";
+    case STA_ERR_NOT_TILE_MULTIPLE: return "latent is not an integer multiple of the tile";
+    case STA_ERR_WINDOW: return "window entries must be at least one tile";
+    case STA_ERR_UNSUPPORTED: return "head_dim, tile volume, head count or dtype not supported";
+    case STA_ERR_ALIGN: return "tensor pointer is not 16-byte aligned";
+    case STA_ERR_HIP: return "HIP runtime error at launch";
+    case STA_ERR_WORKSPACE: return "workspace missing or too small";
+    case STA_ERR_TOO_LARGE: return "size exceeds the 32-bit index range of the kernels";
+    default: return "unknown error code";
+  }
+}
+
+static int tile_copy(const void* src, void* dst, int64_t B, int64_t Hh, int64_t D,
+                     sta_dim3 latent, sta_dim3 tile, sta_dtype dt, void* stream, bool to_tm) {
+  Geometry g;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if (!src || !dst) return STA_ERR_ARG;
+  if ((st = check_sizes(B, Hh, D, g))) return st;
+  const int eb = elem_bytes(dt);
+  if (!eb) return STA_ERR_UNSUPPORTED;
+  if (misaligned(src) || misaligned(dst)) return STA_ERR_ALIGN;
+  if (D * eb >= (1ll << 24)) return STA_ERR_TOO_LARGE;
+  return to_status(launch_tile_copy(src, dst, B * Hh, D * eb, g, to_tm, (hipStream_t)stream));
+}
+
+int sta_tile_reorder(const void* x, void* y, int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
+                     sta_dim3 tile, sta_dtype dt, void* stream) {
+  return tile_copy(x, y, B, Hh, D, latent, tile, dt, stream, true);
+}
+
+int sta_tile_unreorder(const void* y, void* x, int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
+                       sta_dim3 tile, sta_dtype dt, void* stream) {
+  return tile_copy(y, x, B, Hh, D, latent, tile, dt, stream, false);
+}
+
+int64_t sta_tile_pairs_count(sta_dim3 latent, sta_dim3 tile, const int32_t* win_host, int64_t Hh) {
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  int64_t n = 0;
+  for (int64_t h = 0; h < Hh; ++h) n += (int64_t)g.ntiles * ht.wp[h][0] * ht.wp[h][1] * ht.wp[h][2];
+  return n;
+}
+
+static void fill_offsets(int64_t* off, const Geometry& g, const HeadTable& ht, int64_t Hh) {
+  off[0] = 0;
+  for (int64_t h = 0; h < Hh; ++h)
+    off[h + 1] = off[h] + (int64_t)g.ntiles * ht.wp[h][0] * ht.wp[h][1] * ht.wp[h][2];
+}
+
+int sta_tile_pairs(int32_t* pairs_dev, int64_t* head_offsets_host, sta_dim3 latent, sta_dim3 tile,
+                   const int32_t* win_host, int64_t Hh, int transpose, void* stream) {
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  if (!pairs_dev) return STA_ERR_ARG;
+  if (Hh * (int64_t)g.ntiles >= (1ll << 31)) return STA_ERR_TOO_LARGE;
+  if (head_offsets_host) fill_offsets(head_offsets_host, g, ht, Hh);
+  return to_status(launch_tile_pairs(pairs_dev, g, ht, (int)Hh, transpose ? 1 : 0,
+                                     (hipStream_t)stream));
+}
+
+int sta_tile_pairs_host(int32_t* pairs_host, int64_t* head_offsets_host, sta_dim3 latent,
+                        sta_dim3 tile, const int32_t* win_host, int64_t Hh, int transpose) {
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  if (!pairs_host) return STA_ERR_ARG;
+  if (head_offsets_host) fill_offsets(head_offsets_host, g, ht, Hh);
+  host_tile_pairs(pairs_host, g, ht, (int)Hh, transpose ? 1 : 0);
+  return STA_OK;
+}
+
+static int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t Hh, int64_t D, const Geometry& g, const HeadTable& ht,
+                        float scale, sta_dtype dt, void* stream) {
+  if (!q || !k || !v || !o) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
+  int st = check_sizes(B, Hh, D, g);
+  if (st) return st;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return STA_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  if (dt == STA_BF16) {
+    if (!fwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
+    return to_status(launch_fwd_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                     (uint16_t*)o, lse, g, ht, (int)B, (int)Hh, (int)D, scale, s));
+  }
+  if (dt == STA_F32) {
+    if (D != 32 && D != 64 && D != 128) return STA_ERR_UNSUPPORTED;
+    return to_status(launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o,
+                                    lse, g, ht, (int)B, (int)Hh, (int)D, scale, s));
+  }
+  return STA_ERR_UNSUPPORTED;
+}
+
+int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
+                float scale, sta_dtype dt, void* stream) {
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  return forward_impl(q, k, v, o, lse, B, Hh, D, g, ht, scale, dt, stream);
+}
+
+size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
+                                    sta_dtype dt) {
+  (void)D;
+  (void)dt;
+  if (B < 1 || Hh < 1 || latent.t < 1 || latent.h < 1 || latent.w < 1) return 0;
+  return (size_t)B * Hh * latent.t * latent.h * latent.w * sizeof(float);
+}
+
+int sta_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                 int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                 const int32_t* win_host, float scale, sta_dtype dt, void* stream) {
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
+  if ((st = check_sizes(B, Hh, D, g))) return st;
+  if (!workspace || ws_bytes < sta_backward_workspace_bytes(B, Hh, D, latent, dt))
+    return STA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return STA_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  if (dt == STA_BF16) {
+    if (!bwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
+    return to_status(launch_bwd_bf16(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+        (const uint16_t*)dout, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, (float*)workspace,
+        g, ht, (int)B, (int)Hh, (int)D, scale, s));
+  }
+  if (dt == STA_F32) {
+    if (D != 32 && D != 64 && D != 128) return STA_ERR_UNSUPPORTED;
+    return to_status(launch_bwd_f32((const float*)q, (const float*)k, (const float*)v,
+                                    (const float*)o, (const float*)dout, lse, (float*)dq,
+                                    (float*)dk, (float*)dv, (float*)workspace, g, ht, (int)B,
+                                    (int)Hh, (int)D, scale, s));
+  }
+  return STA_ERR_UNSUPPORTED;
+}
+
+int sta_dense_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t Hh, int64_t S, int64_t D, float scale, sta_dtype dt, void* stream) {
+  if (S < 1 || S >= (1ll << 31)) return S < 1 ? STA_ERR_ARG : STA_ERR_TOO_LARGE;
+  // Dense attention is the window rule on a 1 x 1 x (S/Lt) grid of Lt-token
+  // tiles with a window spanning the whole grid.
+  int64_t Lt;
+  if (dt == STA_BF16) {
+    if (S % 384 == 0) Lt = 384;
+    else if (S % 128 == 0) Lt = 128;
+    else if (S % 32 == 0) Lt = 32;
+    else return STA_ERR_UNSUPPORTED;
+  } else {
+    Lt = S;
+  }
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(sta_dim3{1, 1, (int32_t)S}, sta_dim3{1, 1, (int32_t)Lt}, &g);
+  if (st) return st;
+  if (Hh < 1) return STA_ERR_ARG;
+  if (Hh > STA_MAX_HEADS) return STA_ERR_UNSUPPORTED;
+  std::vector<int32_t> win(3 * Hh);
+  for (int64_t h = 0; h < Hh; ++h) {
+    win[3 * h] = 1;
+    win[3 * h + 1] = 1;
+    win[3 * h + 2] = g.n2;
+  }
+  if ((st = make_heads(win.data(), Hh, g, &ht))) return st;
+  return forward_impl(q, k, v, o, lse, B, Hh, D, g, ht, scale, dt, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Internal launcher declarations shared by the kernel sources and the C-ABI.
+#pragma once
+
+#include "sta_common.h"
+
+namespace sta {
+
+// Reorder (to_tile_major) or unreorder of BH = B*Hh sequences of S rows.
+hipError_t launch_tile_copy(const void* src, void* dst, int64_t BH, int64_t row_bytes,
+                            const Geometry& g, bool to_tile_major, hipStream_t stream);
+
+hipError_t launch_tile_pairs(int32_t* out, const Geometry& g, const HeadTable& ht, int Hh,
+                             int transpose, hipStream_t stream);
+void host_tile_pairs(int32_t* out, const Geometry& g, const HeadTable& ht, int Hh, int transpose);
+
+// fp32 debug instance (D in {32, 64, 128}).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
+                          float scale, hipStream_t stream);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* dl, const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
+                          float scale, hipStream_t stream);
+
+// bf16 MFMA instance (D in {64, 128}, L % 32 == 0).
+bool fwd_bf16_supported(int D, int L);
+hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
+                           int D, float scale, hipStream_t stream);
+bool bwd_bf16_supported(int D, int L);
+hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* o, const uint16_t* dout, const float* lse,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dl,
+                           const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
+                           float scale, hipStream_t stream);
+
+}  // namespace sta

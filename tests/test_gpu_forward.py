@@ -1,0 +1,220 @@
+"""GPU parity of the libsta kernels against the fp64 CPU oracle (through the C-ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from _helpers import bits, err_report, sample_query_tiles, to64
+from sparse_sliding_tile_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2     # max-abs, bf16 I/O with fp32 accumulation
+F32_TOL = 1e-5      # max-abs, fp32 debug instance
+BF16_REL_RMS = 1e-2
+
+
+@pytest.fixture(scope="module")
+def sta():
+    import sparse_sliding_tile_amd as s
+    s.lib()
+    return s
+
+
+def _dev(x):
+    return x.to("cuda").contiguous()
+
+
+# ------------------------------------------------------------------ reorder
+
+REORDER_CASES = [((6, 16, 16), (2, 4, 4), 1, 2, 64, torch.float32),
+                 ((6, 16, 16), (2, 4, 4), 2, 3, 128, torch.bfloat16),
+                 ((5, 6, 10), (5, 3, 2), 1, 2, 24, torch.bfloat16),     # ragged rows: 48-byte tokens
+                 ((3, 4, 5), (1, 1, 1), 2, 1, 7, torch.float32),       # 28-byte rows, identity order
+                 ((30, 48, 80), (6, 8, 8), 1, 2, 128, torch.bfloat16)]
+
+
+@pytest.mark.parametrize("latent,tile,B,Hh,D,dtype", REORDER_CASES)
+def test_reorder_bit_exact(sta, latent, tile, B, Hh, D, dtype):
+    S = int(np.prod(latent))
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn((B, Hh, S, D), generator=g).to(dtype)
+    y = sta.tile_reorder(_dev(x), latent, tile)
+    ref = O.reorder(bits(x), latent, tile)
+    assert np.array_equal(bits(y), ref)
+    back = sta.tile_unreorder(y, latent, tile)
+    assert np.array_equal(bits(back), bits(x))
+
+
+def test_reorder_full_size_sampled(sta):
+    """Wan-sized tensor [1, 40, 92160, 128] bf16: every sampled raster row lands
+    at its oracle position, and the round trip is the identity."""
+    latent, tile = (24, 48, 80), (6, 8, 8)
+    S = int(np.prod(latent))
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn((1, 40, S, 128), generator=g).to(torch.bfloat16)
+    xd = _dev(x)
+    y = sta.tile_reorder(xd, latent, tile)
+    pi = O.tile_major_index(latent, tile)
+    rows = np.random.default_rng(0).choice(S, 4096, replace=False)
+    got = bits(y[:, :, torch.from_numpy(pi[rows]).cuda()])
+    assert np.array_equal(got, bits(x[:, :, torch.from_numpy(rows)]))
+    back = sta.tile_unreorder(y, latent, tile)
+    assert torch.equal(back.view(torch.int16), xd.view(torch.int16))
+
+
+# ------------------------------------------------------------------ pairs
+
+PAIR_CASES = [((6, 16, 16), (2, 4, 4), [(3, 3, 3), (1, 2, 5)]),
+              ((30, 48, 80), (6, 8, 8), I.mixed_windows(24, 0)),
+              ((24, 48, 80), (6, 8, 8), [(3, 3, 5)] * 3),
+              ((24, 64, 64), (6, 8, 8), [(3, 5, 5)] * 2)]
+
+
+@pytest.mark.parametrize("latent,tile,wins", PAIR_CASES)
+@pytest.mark.parametrize("transpose", [False, True])
+def test_tile_pairs_bit_exact(sta, latent, tile, wins, transpose):
+    p, off = sta.tile_pairs(latent, tile, wins, transpose=transpose)
+    rp, roff = O.tile_pairs(latent, tile, wins, transpose=transpose)
+    assert np.array_equal(off, roff)
+    assert np.array_equal(p.cpu().numpy(), rp)
+
+
+# ------------------------------------------------------------------ forward, fp32 debug
+
+def _tile_major(sta, t, latent, tile):
+    return sta.tile_reorder(_dev(t), latent, tile)
+
+
+def test_forward_f32_tiny(sta):
+    w = I.WORKLOADS["tiny_f32"]
+    x = I.workload_inputs("tiny_f32")
+    latent, tile, wins = w["latent"], w["tile"], w["windows"]
+    q, k, v = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v"))
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=64 ** -0.5)
+    rq, rk, rv = (O.reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
+    ro, rl = O.forward(rq, rk, rv, latent, tile, wins, 64 ** -0.5)
+    assert err_report(to64(o), ro)["max_abs"] < F32_TOL
+    assert err_report(to64(lse), rl)["max_abs"] < F32_TOL
+    # the same result in raster order after unreorder
+    ro_r, _ = O.forward(to64(x["q"]), to64(x["k"]), to64(x["v"]), latent, tile, wins, 64 ** -0.5,
+                        order="raster")
+    assert err_report(to64(sta.tile_unreorder(o, latent, tile)), ro_r)["max_abs"] < F32_TOL
+
+
+def test_backward_f32_tiny(sta):
+    w = I.WORKLOADS["tiny_f32"]
+    x = I.workload_inputs("tiny_f32", with_do=True)
+    latent, tile = w["latent"], w["tile"]
+    wins = [(3, 3, 3), (1, 2, 4)]
+    scale = 64 ** -0.5
+    q, k, v, do = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v", "do"))
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
+    dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
+    rq, rk, rv, rdo = (O.reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v", "do"))
+    ref = O.backward(rq, rk, rv, rdo, latent, tile, wins, scale)
+    for got, r in zip((dq, dk, dv), ref):
+        assert err_report(to64(got), r)["max_abs"] < F32_TOL
+
+
+# ------------------------------------------------------------------ forward, bf16 MFMA
+
+BF16_SMALL = [  # latent, tile, B, windows, D   (tile volume 32 and 128; several tiles; batch 2)
+    ((6, 16, 16), (2, 4, 4), 2, [(3, 3, 3), (1, 2, 5), (9, 9, 9)], 128),
+    ((6, 16, 16), (2, 4, 4), 1, [(2, 3, 1), (3, 1, 3)], 64),
+    ((6, 32, 32), (2, 8, 8), 2, [(3, 3, 3), (1, 1, 1), (3, 2, 4)], 128),
+    ((12, 16, 24), (6, 8, 8), 1, [(1, 3, 3), (2, 2, 2)], 128),        # L = 384
+    ((6, 32, 32), (2, 8, 8), 1, [(3, 3, 3), (1, 4, 2)], 64),
+]
+
+
+@pytest.mark.parametrize("latent,tile,B,wins,D", BF16_SMALL)
+def test_forward_bf16_small(sta, latent, tile, B, wins, D):
+    S = int(np.prod(latent))
+    x = I.make_inputs(B, len(wins), S, D, "bf16", seed=5)
+    scale = D ** -0.5
+    q, k, v = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v"))
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
+    rq, rk, rv = (O.reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
+    ro, rl = O.forward(rq, rk, rv, latent, tile, wins, scale)
+    eo, el = err_report(to64(o), ro), err_report(to64(lse), rl)
+    print("O", eo, "LSE", el)
+    assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+    assert el["max_abs"] < BF16_TOL
+
+
+def test_forward_bf16_zero_query_window_mean(sta):
+    """Q = 0: every output row is the plain mean of V over its window, which
+    pins window membership far more tightly than the 2e-2 tolerance."""
+    latent, tile, wins = (6, 32, 32), (2, 8, 8), [(3, 3, 3), (1, 2, 4)]
+    S = int(np.prod(latent))
+    x = I.make_inputs(1, 2, S, 128, "bf16", seed=6)
+    q = torch.zeros((1, 2, S, 128), dtype=torch.bfloat16, device="cuda")
+    k, v = (_tile_major(sta, x[n], latent, tile) for n in ("k", "v"))
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=0.088)
+    ro, rl = O.forward(np.zeros((1, 2, S, 128)), to64(k), to64(v), latent, tile, wins, 0.088)
+    e = err_report(to64(o), ro)
+    print(e)
+    assert e["max_abs"] < 4e-3
+    assert err_report(to64(lse), rl)["max_abs"] < 1e-4
+
+
+def _check_sampled(sta, name, heads, rows_per_tile=32, seed=0):
+    w = I.WORKLOADS[name]
+    latent, tile, wins, D = w["latent"], w["tile"], w["windows"], w["head_dim"]
+    n, L = O.tile_grid(latent, tile)
+    x = I.workload_inputs(name)
+    scale = D ** -0.5
+    q, k, v = (_tile_major(sta, x[nm], latent, tile) for nm in ("q", "k", "v"))
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
+    torch.cuda.synchronize()
+    tiles = sample_query_tiles(n, 1, seed)
+    rows = np.concatenate([np.r_[a * L:a * L + rows_per_tile // 2, (a + 1) * L - rows_per_tile // 2:(a + 1) * L]
+                           for a in tiles])
+    rt = torch.from_numpy(rows).cuda()
+    worst = {}
+    for h in heads:
+        hq, hk, hv = (to64(t[:, h:h + 1]) for t in (q, k, v))
+        ro, rl = O.forward(hq, hk, hv, latent, tile, [wins[h]], scale, rows=rows)
+        eo = err_report(to64(o[:, h:h + 1, rt]), ro)
+        el = err_report(to64(lse[:, h:h + 1, rt]), rl)
+        print(name, "head", h, wins[h], "O", eo, "LSE", el)
+        assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+        assert el["max_abs"] < BF16_TOL
+        worst[h] = eo
+    return worst
+
+
+def test_forward_bf16_hunyuan_uniform_sampled(sta):
+    _check_sampled(sta, "hunyuan_30x48x80_w333", heads=[0, 11, 23])
+
+
+def test_forward_bf16_hunyuan_mixed_sampled(sta):
+    wins = I.WORKLOADS["hunyuan_30x48x80_mixed"]["windows"]
+    heads = sorted({wins.index(wd) for wd in set(wins)})   # one head of every window kind drawn
+    _check_sampled(sta, "hunyuan_30x48x80_mixed", heads=heads, rows_per_tile=16)
+
+
+def test_forward_bf16_wan_sampled(sta):
+    _check_sampled(sta, "wan_24x48x80_w335", heads=[0, 39])
+
+
+# ------------------------------------------------------------------ dense
+
+def test_dense_bf16_small(sta):
+    x = I.make_inputs(1, 2, 1536, 128, "bf16", seed=7)
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sta.dense_forward(q, k, v, scale=128 ** -0.5)
+    ro, rl = O.dense_forward(to64(q), to64(k), to64(v), 128 ** -0.5)
+    eo = err_report(to64(o), ro)
+    assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+    assert err_report(to64(lse), rl)["max_abs"] < BF16_TOL
+
+
+def test_dense_f32_small(sta):
+    x = I.make_inputs(1, 2, 640, 64, "f32", seed=8)
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sta.dense_forward(q, k, v, scale=0.125)
+    ro, rl = O.dense_forward(to64(q), to64(k), to64(v), 0.125)
+    assert err_report(to64(o), ro)["max_abs"] < F32_TOL
+    assert err_report(to64(lse), rl)["max_abs"] < F32_TOL
