@@ -1,0 +1,94 @@
+// MFMA, LDS and cross-lane building blocks shared by the bf16 attention kernels.
+//
+// Lane layouts of v_mfma_f32_32x32x16_bf16 (A: 32x16, B: 16x32, C: 32x32 fp32)
+// for lane l, g = l / 32, c = l % 32:
+//   A: 8 bf16  A[c][8g .. 8g+7]
+//   B: 8 bf16  B[8g .. 8g+7][c]
+//   C: 16 fp32 C[8i + 4g + j][c] at element 4i + j
+// ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: if lane j = 4r + s
+// of a group reads the 4 bf16 M[j][0..3], lane i of the group receives
+// (M[i/4][i%4], M[4 + i/4][i%4], M[8 + i/4][i%4], M[12 + i/4][i%4]).  Four lanes
+// reading 4 consecutive values each of row r therefore hand lane i the values of
+// 4 rows at one column: a transposed operand read from a row-major tile.
+#pragma once
+
+#include "sta_common.h"
+
+namespace sta {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row-major bf16 tiles in LDS with D/8 16-byte chunks per row.  Chunk c of row
+// r is stored at chunk position c ^ swz(r).  swz maps any 8 consecutive rows to
+// 8 distinct values (so 8 lanes reading one chunk of 8 rows with 16-byte reads
+// hit all 32 banks once) and any 4 consecutive rows starting at a multiple of 4
+// to 4 values of distinct even part (so a 16-lane transposed read of 4 rows x
+// 2 adjacent chunks also covers all 32 banks).
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r & 3u) << 1) | ((r >> 2) & 1u); }
+
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(uint32_t r, uint32_t chunk) {  // bytes
+  return r * (D * 2) + ((chunk ^ swz(r)) << 4);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
+  return *(const u32x4*)(base + off);
+}
+
+// Transposed 8-byte read (see the layout note above).
+__device__ __forceinline__ s16x4 lds_read_tr(const char* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(s16x4 lo, s16x4 hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l writes bytes
+// [16 l, 16 l + 16) of the 1 KiB LDS segment starting at lds (wave-uniform).
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// x combined with the value of lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float xmax32(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xsum32(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Copies a [rows x D] bf16 tile (rows consecutive sequence rows starting at
+// grow) into LDS in the swizzled layout with 16-byte DMA; the NW waves of the
+// workgroup split the 1 KiB segments.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, size_t grow, char* lds,
+                                         int wave, int lane) {
+  constexpr int RPS = 1024 / (D * 2);       // rows per 1 KiB segment
+  constexpr int SEGS = ROWS / RPS;          // segments per tile
+  static_assert(SEGS % NW == 0, "tile does not split over the waves");
+  constexpr int CPR = D / 8;                // chunks per row
+#pragma unroll
+  for (int e = 0; e < SEGS / NW; ++e) {
+    const int seg = wave * (SEGS / NW) + e;
+    const int r = seg * RPS + lane / CPR;
+    const int p = lane % CPR;
+    const int c = p ^ (int)swz(r);
+    dma16(g + (grow + r) * D + c * 8, lds + seg * 1024);
+  }
+}
+
+}  // namespace sta
