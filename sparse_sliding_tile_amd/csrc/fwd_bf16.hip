@@ -37,47 +37,69 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int QT, int NW, int KB>
+template <int D, int QT, int NW>
 struct FwdCfg {
+  static constexpr int KB = 32;              // keys per LDS stage (one MFMA sub-tile)
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROWS = NW * QT * 32;  // query rows per workgroup
   static constexpr int KS = D / 16;          // MFMA k-steps of K Q^T
   static constexpr int DT = D / 32;          // 32-wide d tiles of O^T
-  static constexpr int KT = KB / 32;         // 32-key sub-tiles per block
   static constexpr int TILE_BYTES = KB * D * 2;
 };
 
-// One key block: S^T, online softmax, O^T update.
-template <int D, int QT, int KB>
-__device__ __forceinline__ void attend_block(const char* kl, const char* vl,
-                                             const bf16x8 (&qf)[QT][D / 16],
-                                             f32x16 (&oacc)[QT][D / 32], float (&mrun)[QT],
-                                             float (&lrun)[QT], float c_log2, int lane) {
-  constexpr int KS = D / 16, DT = D / 32, KT = KB / 32;
-  const int grp = lane >> 5, c32 = lane & 31;
+// K operand fragments of one 32-key stage: lane holds 8 d of key row c32.
+template <int D>
+__device__ __forceinline__ void read_k(const char* kl, bf16x8 (&kf)[D / 16], int grp, int c32) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    kf[ks] = as_bf16x8(lds_read16(kl, tile_off<D>(c32, ks * 2 + grp)));
+}
 
-  f32x16 sacc[KT][QT];
+// V^T operand fragments of one 32-key stage, read transposed from the
+// row-major V tile: lane i of each 16-lane group takes d = dt*32 + 16h + i and
+// keys (16s + 4g + r) and (16s + 8 + 4g + r), r = 0..3.
+template <int D>
+__device__ __forceinline__ void read_vt(const char* vl, bf16x8 (&vf)[D / 32][2], int lane) {
+  const int grp = lane >> 5, l16 = lane & 15, h = (lane >> 4) & 1;
+  const int vr = grp * 4 + (l16 >> 2);
+  const int vc = l16 & 3;
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int d = dt * 32 + 16 * h + 4 * vc;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = as_bf16x8(lds_read16(kl, tile_off<D>(kt * 32 + c32, ks * 2 + grp)));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma32(a, qf[qt][ks], sacc[kt][qt]);
+    for (int s = 0; s < 2; ++s) {
+      const int r0 = 16 * s + vr;
+      const s16x4 lo = lds_read_tr(vl, tile_off<D>(r0, d >> 3) + (d & 4) * 2);
+      const s16x4 hi = lds_read_tr(vl, tile_off<D>(r0 + 8, d >> 3) + (d & 4) * 2);
+      vf[dt][s] = join_tr(lo, hi);
     }
   }
+}
 
+// S^T = K Q^T for one 32-key stage.
+template <int D, int QT>
+__device__ __forceinline__ void qk_stage(const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[QT][D / 16],
+                                         f32x16 (&sacc)[QT]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) sacc[qt] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) sacc[qt] = mfma32(kf[ks], qf[qt][ks], sacc[qt]);
+}
+
+// Online softmax of one stage (lazy rescale), producing the bf16 P^T operand.
+template <int D, int QT>
+__device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (&pf)[QT][2],
+                                              f32x16 (&oacc)[QT][D / 32], float (&mrun)[QT],
+                                              float (&lrun)[QT], float c_log2) {
   bool need = false;
   float mblk[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float mx = sacc[0][qt][0];
+    float mx = sacc[qt][0];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][qt][e]);
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[qt][e]);
     mblk[qt] = xmax32(mx) * c_log2;
     need |= mblk[qt] > mrun[qt] + kRescaleThreshold;
   }
@@ -89,71 +111,73 @@ __device__ __forceinline__ void attend_block(const char* kl, const char* vl,
       mrun[qt] = mn;
       lrun[qt] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[qt][dt][e] *= alpha;
     }
   }
-  bf16x8 pf[QT][KT][2];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float mneg = -mrun[qt];
     float ls = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][8 * s + e], c_log2, mneg));
-          ls += p;
-          pf[qt][kt][s][e] = (__bf16)p;
-        }
-    lrun[qt] += ls;
-  }
-
-  // V^T operand: lane i of each 16-lane group takes d = dt*32 + 16h + i and
-  // keys (16s + 4g + r) and (16s + 8 + 4g + r), r = 0..3.
-  const int l16 = lane & 15, h = (lane >> 4) & 1;
-  const int vr = grp * 4 + (l16 >> 2);  // row inside the 16-key step
-  const int vc = l16 & 3;               // 4-value group inside the 16 d
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int d = dt * 32 + 16 * h + 4 * vc;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int r0 = kt * 32 + 16 * s + vr;
-        const s16x4 lo = lds_read_tr(vl, tile_off<D>(r0, d >> 3) + (d & 4) * 2);
-        const s16x4 hi = lds_read_tr(vl, tile_off<D>(r0 + 8, d >> 3) + (d & 4) * 2);
-        const bf16x8 a = join_tr(lo, hi);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma32(a, pf[qt][kt][s], oacc[qt][dt]);
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qt][8 * s + e], c_log2, mneg));
+        ls += p;
+        pf[qt][s][e] = (__bf16)p;
       }
+    lrun[qt] += ls;
   }
 }
 
-template <int D, int QT, int NW, int KB, int OCC>
+// O^T += V^T P^T for one stage.
+template <int D, int QT>
+__device__ __forceinline__ void pv_stage(const bf16x8 (&vf)[D / 32][2], const bf16x8 (&pf)[QT][2],
+                                         f32x16 (&oacc)[QT][D / 32]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma32(vf[dt][s], pf[qt][s], oacc[qt][dt]);
+}
+
+template <int D, int QT, int NW, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, Geometry g,
-    HeadTable ht, int B, int Hh, float c_log2, int blocks_per_tile, int total) {
-  using C = FwdCfg<D, QT, NW, KB>;
-  // Two buffers as distinct objects, so the compiler can tell the DMA target
-  // of the next block from the buffer being read.
+    HeadTable ht, int B, int Hh, float c_log2, int blocks_per_tile, int total, int group_items) {
+  using C = FwdCfg<D, QT, NW>;
+  constexpr int KB = C::KB;
+  // A ring of three stages, each buffer its own object so the compiler can
+  // tell the DMA target from the buffers being read.
   __shared__ __attribute__((aligned(1024))) char kl0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vl0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kl1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vl1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kl2[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vl2[C::TILE_BYTES];
 
-  // Work item: workgroups go round-robin to the 8 XCDs; remap so that XCD x
-  // walks one contiguous run of (head, query tile) items and its L2 sees
-  // neighbouring windows.
+  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (XCD x runs
+  // every 8th blockIdx).  Items are ordered (head slot, batch, query tile,
+  // sub-block); consecutive groups of group_items items (one or a few whole
+  // (head, batch) sequences, a multiple of 8) are split into 8 contiguous
+  // chunks, chunk x going to XCD x.  So all XCDs work on the same few heads at
+  // a time (their K/V stays in the shared last-level cache) and each XCD walks
+  // neighbouring query tiles (its L2 sees overlapping windows).  group_items ==
+  // 0 (no such grouping exists) falls back to one contiguous range per XCD.
   const uint32_t bid = blockIdx.x;
   const uint32_t xcd = bid & 7u, local = bid >> 3;
-  const uint32_t per = (uint32_t)total >> 3, rem = (uint32_t)total & 7u;
-  uint32_t item = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  uint32_t item;
+  if (group_items > 0) {
+    const uint32_t per_x = (uint32_t)group_items >> 3;
+    item = (local / per_x) * (uint32_t)group_items + xcd * per_x + local % per_x;
+  } else {
+    const uint32_t per = (uint32_t)total >> 3, rem = (uint32_t)total & 7u;
+    item = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  }
   const int sub = item % blocks_per_tile;
   item /= blocks_per_tile;
   const int qtile = item % g.ntiles;
@@ -203,9 +227,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     return key0;
   };
   auto issue = [&](char* kl, char* vl) {
-    const int key0 = next_key0();
-    dma_tile<D, KB, NW>(kb, (size_t)key0, kl, wave, lane);
-    dma_tile<D, KB, NW>(vb, (size_t)key0, vl, wave, lane);
+    dma_kv<D, KB, NW>(kb, vb, (size_t)next_key0(), kl, vl, wave, lane);
   };
 
   f32x16 oacc[QT][C::DT];
@@ -218,19 +240,39 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     lrun[qt] = 0.f;
   }
 
+  // Pipeline: stage j sits in buffer j % 3.  While the MFMAs of stage j run,
+  // the V^T fragments of stage j (before Q K^T) and the K fragments of stage
+  // j + 1 (before P V) are read from LDS, and stage j + 2 is in flight from
+  // HBM.  The barrier between softmax and P V publishes stage j + 1 and frees
+  // buffer (j + 2) % 3, whose last reader was the P V of stage j - 1.
   issue(kl0, vl0);
+  if (nblk > 1) issue(kl1, vl1);
   wait_dma();
   __syncthreads();
-  for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) issue(kl1, vl1);
-    attend_block<D, QT, KB>(kl0, vl0, qf, oacc, mrun, lrun, c_log2, lane);
-    wait_dma();
-    __syncthreads();
-    if (blk + 1 >= nblk) break;
-    if (blk + 2 < nblk) issue(kl0, vl0);
-    attend_block<D, QT, KB>(kl1, vl1, qf, oacc, mrun, lrun, c_log2, lane);
-    wait_dma();
-    __syncthreads();
+  bf16x8 kf[C::KS];
+  read_k<D>(kl0, kf, grp, c32);
+
+  auto stage = [&](int j, const char* vl_cur, const char* kl_nxt, char* kl_nn, char* vl_nn) {
+    bf16x8 vf[C::DT][2];
+    read_vt<D>(vl_cur, vf, lane);
+    f32x16 sacc[QT];
+    qk_stage<D, QT>(kf, qf, sacc);
+    bf16x8 pf[QT][2];
+    softmax_stage<D, QT>(sacc, pf, oacc, mrun, lrun, c_log2);
+    if (j + 1 < nblk) {
+      wait_dma();
+      __syncthreads();
+      if (j + 2 < nblk) issue(kl_nn, vl_nn);
+      read_k<D>(kl_nxt, kf, grp, c32);
+    }
+    pv_stage<D, QT>(vf, pf, oacc);
+  };
+  for (int j = 0; j < nblk; j += 3) {
+    stage(j, vl0, kl1, kl2, vl2);
+    if (j + 1 >= nblk) break;
+    stage(j + 1, vl1, kl2, kl0, vl0);
+    if (j + 2 >= nblk) break;
+    stage(j + 2, vl2, kl0, kl1, vl1);
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
@@ -252,16 +294,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   }
 }
 
-template <int D, int QT, int NW, int KB, int OCC>
+// Items per XCD-split group: the smallest number of whole (head, batch)
+// sequences whose item count is a multiple of 8 and divides the total; 0 if
+// there is none.
+inline int xcd_group_items(int seqs, int items_per_seq) {
+  for (int gsz = 1; gsz <= 8; ++gsz)
+    if ((gsz * items_per_seq) % 8 == 0 && seqs % gsz == 0) return gsz * items_per_seq;
+  return 0;
+}
+
+template <int D, int QT, int NW, int OCC>
 hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                       float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                       float scale, hipStream_t st) {
-  using C = FwdCfg<D, QT, NW, KB>;
+  using C = FwdCfg<D, QT, NW>;
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, KB, OCC>), dim3((uint32_t)total),
+  const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC>), dim3((uint32_t)total),
                      dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, B, Hh, scale * kLog2e, bpt,
-                     total);
+                     total, group);
   return hipGetLastError();
 }
 
@@ -274,12 +326,12 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int D, float scale, hipStream_t st) {
   const int L = g.L;
   if (D == 128) {
-    if (L % 128 == 0) return launch_cfg<128, 1, 4, 64, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<128, 1, 1, 32, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    if (L % 128 == 0) return launch_cfg<128, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<128, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
   }
   if (D == 64) {
-    if (L % 128 == 0) return launch_cfg<64, 1, 4, 64, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<64, 1, 1, 32, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    if (L % 128 == 0) return launch_cfg<64, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<64, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
   }
   return hipErrorInvalidValue;
 }

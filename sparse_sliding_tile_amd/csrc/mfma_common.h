@@ -25,17 +25,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Row-major bf16 tiles in LDS with D/8 16-byte chunks per row.  Chunk c of row
-// r is stored at chunk position c ^ swz(r).  swz maps any 8 consecutive rows to
-// 8 distinct values (so 8 lanes reading one chunk of 8 rows with 16-byte reads
-// hit all 32 banks once) and any 4 consecutive rows starting at a multiple of 4
-// to 4 values of distinct even part (so a 16-lane transposed read of 4 rows x
-// 2 adjacent chunks also covers all 32 banks).
-__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r & 3u) << 1) | ((r >> 2) & 1u); }
+// Row-major bf16 tiles in LDS with D/8 16-byte chunks per row; chunk c of row r
+// is stored at chunk position c ^ swz<D>(r).  The gfx950 LDS serves 256 bytes
+// per clock (64 banks): a 16-byte-per-lane read is conflict-free when each 16
+// consecutive lanes touch 16 distinct 16-byte bank groups of a 256-byte line.
+//   D = 128 (256-byte rows): 16 consecutive rows at one chunk -> 16 distinct
+//     positions (K operand reads); rows 4m..4m+3 x 4 adjacent chunks -> 16
+//     distinct positions (transposed V operand reads).
+//   D = 64 (128-byte rows, two rows per line): the same two properties with the
+//     row parity supplying the line half.
+template <int D>
+__device__ __forceinline__ uint32_t swz(uint32_t r) {
+  if constexpr (D == 128) {
+    return ((r & 3u) << 2) | ((r >> 2) & 3u);
+  } else {
+    return (((r >> 1) & 1u) << 2) | ((r >> 2) & 3u);
+  }
+}
 
 template <int D>
 __device__ __forceinline__ uint32_t tile_off(uint32_t r, uint32_t chunk) {  // bytes
-  return r * (D * 2) + ((chunk ^ swz(r)) << 4);
+  return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
@@ -71,23 +81,29 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Copies a [rows x D] bf16 tile (rows consecutive sequence rows starting at
-// grow) into LDS in the swizzled layout with 16-byte DMA; the NW waves of the
-// workgroup split the 1 KiB segments.
+// Copies the K and V blocks [ROWS x D] (ROWS consecutive sequence rows from
+// grow) into LDS in the swizzled layout with 16-byte DMA.  The 1 KiB segments
+// of both tiles are dealt round-robin over the NW waves of the workgroup.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, size_t grow, char* lds,
-                                         int wave, int lane) {
+__device__ __forceinline__ void dma_kv(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+                                       size_t grow, char* kl, char* vl, int wave, int lane) {
   constexpr int RPS = 1024 / (D * 2);       // rows per 1 KiB segment
   constexpr int SEGS = ROWS / RPS;          // segments per tile
-  static_assert(SEGS % NW == 0, "tile does not split over the waves");
+  static_assert(ROWS % RPS == 0, "block rows must fill whole segments");
   constexpr int CPR = D / 8;                // chunks per row
+  constexpr int PER = (2 * SEGS + NW - 1) / NW;
+  const int rin = lane / CPR;
+  const int p = lane % CPR;
 #pragma unroll
-  for (int e = 0; e < SEGS / NW; ++e) {
-    const int seg = wave * (SEGS / NW) + e;
-    const int r = seg * RPS + lane / CPR;
-    const int p = lane % CPR;
-    const int c = p ^ (int)swz(r);
-    dma16(g + (grow + r) * D + c * 8, lds + seg * 1024);
+  for (int e = 0; e < PER; ++e) {
+    const int seg2 = wave + e * NW;
+    if ((2 * SEGS) % NW == 0 || seg2 < 2 * SEGS) {
+      const bool isv = seg2 >= SEGS;
+      const int seg = isv ? seg2 - SEGS : seg2;
+      const int r = seg * RPS + rin;
+      const int c = p ^ (int)swz<D>(r);
+      dma16((isv ? vg : kg) + (grow + r) * D + c * 8, (isv ? vl : kl) + seg * 1024);
+    }
   }
 }
 
