@@ -40,7 +40,7 @@ import numpy as np
 __all__ = [
     "tile_grid", "tile_major_index", "reorder", "unreorder", "window_start",
     "window_contains", "tile_pairs", "token_tile_coords", "window_mask",
-    "forward", "backward", "backward_key_rows", "dense_forward",
+    "forward", "backward", "backward_key_rows", "backward_query_rows", "dense_forward",
 ]
 
 
@@ -164,15 +164,17 @@ def token_tile_coords(latent, tile, order="tile"):
     raise ValueError("order is 'tile' or 'raster'")
 
 
-def window_mask(latent, tile, win, order="tile", rows=None):
+def window_mask(latent, tile, win, order="tile", rows=None, cols=None):
     """Boolean mask M[i, j]: key position j is visible to query position i.
 
     [STA-meth]: visibility is decided per tile pair, so every block of the mask
-    is all-true or all-false.  ``rows`` restricts the query positions.
+    is all-true or all-false.  ``rows`` / ``cols`` restrict the query / key
+    positions.
     """
     n, _ = tile_grid(latent, tile)
-    kc = token_tile_coords(latent, tile, order)
-    qc = kc if rows is None else kc[np.asarray(rows)]
+    tc = token_tile_coords(latent, tile, order)
+    qc = tc if rows is None else tc[np.asarray(rows)]
+    kc = tc if cols is None else tc[np.asarray(cols)]
     m = np.ones((qc.shape[0], kc.shape[0]), dtype=bool)
     for d in range(3):
         wp = min(int(win[d]), n[d])
@@ -263,13 +265,7 @@ def backward_key_rows(q, k, v, do, latent, tile, win, scale, b, h, key_rows, ord
     key_rows = np.asarray(key_rows)
     qf, kf, vf, dof = (np.asarray(a[b, h], dtype=np.float64) for a in (q, k, v, do))
     S = qf.shape[0]
-    seen = window_mask(latent, tile, win, order)[:, key_rows].any(axis=1) if S <= 8192 else None
-    if seen is None:  # large grids: test visibility tile-wise, one query tile at a time
-        seen = np.zeros(S, dtype=bool)
-        for c0 in range(0, S, 1024):
-            r = np.arange(c0, min(S, c0 + 1024))
-            seen[r] = window_mask(latent, tile, win, order, rows=r)[:, key_rows].any(axis=1)
-    qi = np.nonzero(seen)[0]
+    qi = np.nonzero(window_mask(latent, tile, win, order, cols=key_rows).any(axis=1))[0]
     dk = np.zeros((key_rows.size, qf.shape[1]))
     dv = np.zeros_like(dk)
     for c0 in range(0, qi.size, 512):
@@ -286,6 +282,30 @@ def backward_key_rows(q, k, v, do, latent, tile, win, scale, b, h, key_rows, ord
         dk += scale * (ds.T @ qf[r])
         dv += pj.T @ dof[r]
     return dk, dv
+
+
+def backward_query_rows(q, k, v, do, latent, tile, win, scale, b, h, rows, order="tile"):
+    """dQ of one (batch b, head h) at the query positions ``rows``.
+
+    Same formulas as ``backward``, row by row: each sampled query's softmax row
+    over its visible keys gives P_i and O_i, then Dl_i = <dO_i, O_i>,
+    dS_ij = P_ij (<dO_i, v_j> - Dl_i) and dQ_i = scale sum_j dS_ij k_j.
+    """
+    rows = np.asarray(rows)
+    qf, kf, vf, dof = (np.asarray(a[b, h], dtype=np.float64) for a in (q, k, v, do))
+    out = np.zeros((rows.size, qf.shape[1]))
+    for c0 in range(0, rows.size, 256):
+        r = rows[c0:c0 + 256]
+        m = window_mask(latent, tile, win, order, rows=r)
+        s = scale * (qf[r] @ kf.T)
+        s[~m] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ vf
+        dl = (dof[r] * o).sum(axis=1, keepdims=True)
+        ds = p * (dof[r] @ vf.T - dl)
+        out[c0:c0 + r.size] = scale * (ds @ kf)
+    return out
 
 
 def dense_forward(q, k, v, scale, rows=None, chunk=256):

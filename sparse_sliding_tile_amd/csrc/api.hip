@@ -202,7 +202,8 @@ size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 l
   (void)D;
   (void)dt;
   if (B < 1 || Hh < 1 || latent.t < 1 || latent.h < 1 || latent.w < 1) return 0;
-  return (size_t)B * Hh * latent.t * latent.h * latent.w * sizeof(float);
+  // Per query row: Dl = <dO, O> and LSE * log2(e), fp32.
+  return 2 * (size_t)B * Hh * latent.t * latent.h * latent.w * sizeof(float);
 }
 
 int sta_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -1,17 +1,386 @@
-// STA backward, bf16 in/out (placeholder until the MFMA kernels land).
+// STA backward, bf16 in/out, fp32 accumulation, on gfx950 MFMA.
+//
+// The gradient of the forward in fwd_bf16.hip ("Sliding Tile Attention",
+// arXiv 2502.04507 summary page: the method is fine-tuned, which needs it).
+// With P the window-masked softmax recomputed from the forward's LSE,
+//   Dl_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Dl_i),
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
+// Three launches, no atomics, deterministic:
+//   1. prep:  Dl and LSE * log2(e) per query row, into the workspace.
+//   2. dQ:    query-tile-major, walking the window like the forward:
+//             S^T = K Q^T, dP^T = V dO^T (lane = query), dQ^T += K^T dS^T.
+//   3. dK/dV: key-tile-major, walking the query tiles whose window holds the
+//             key tile (an interval per dimension): S = Q K^T, dP = dO V^T
+//             (lane = key), dV += P^T dO, dK += dS^T Q.
+// Every (query tile, key tile) pair is a full dense block, as in the forward.
+// The operand layouts, LDS swizzle and transposed reads are those of
+// mfma_common.h; a transposed read of a row-major [32 x D] tile gives the
+// operand [d][row] with the row order of the accumulator (see fwd_bf16.hip).
 #include "kernels.h"
+#include "mfma_common.h"
 
 namespace sta {
 
-bool bwd_bf16_supported(int D, int L) {
-  (void)D;
-  (void)L;
-  return false;
+namespace {
+
+constexpr int kStage = 32;  // rows (keys or queries) per pipeline stage
+
+// --------------------------------------------------------------------------
+// 1. prep: Dl_i = <dO_i, O_i> (fp32) and lse2_i = LSE_i * log2(e).
+//    D/8 lanes per row, 16-byte loads, shuffle reduction.
+// --------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ lse2,
+                                                       float* __restrict__ dl, size_t rows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int c = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)(o + row * D + c * 8);
+    const u32x4 b = *(const u32x4*)(dout + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), s);
+      s = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), s);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (row < rows && c == 0) {
+    dl[row] = s;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
-hipError_t launch_bwd_bf16(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
-                           const uint16_t*, const float*, uint16_t*, uint16_t*, uint16_t*, float*,
-                           const Geometry&, const HeadTable&, int, int, int, float, hipStream_t) {
+// Work item decode shared by both kernels (see the forward for the XCD split).
+__device__ __forceinline__ uint32_t work_item(int total, int group_items) {
+  const uint32_t bid = blockIdx.x;
+  const uint32_t xcd = bid & 7u, local = bid >> 3;
+  if (group_items > 0) {
+    const uint32_t per_x = (uint32_t)group_items >> 3;
+    return (local / per_x) * (uint32_t)group_items + xcd * per_x + local % per_x;
+  }
+  const uint32_t per = (uint32_t)total >> 3, rem = (uint32_t)total & 7u;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 contract_rows(const bf16x8 (&a)[D / 16], const bf16x8 (&b)[D / 16]) {
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(a[ks], b[ks], acc);
+  return acc;
+}
+
+// --------------------------------------------------------------------------
+// 2. dQ (query-major).  Workgroup = NW waves x 32 query rows of one tile.
+// --------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dq,
+    Geometry g, HeadTable ht, int B, int Hh, float c_log2, float scale, int blocks_per_tile,
+    int total, int group_items) {
+  constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2;
+  __shared__ __attribute__((aligned(1024))) char kl0[TB];
+  __shared__ __attribute__((aligned(1024))) char vl0[TB];
+  __shared__ __attribute__((aligned(1024))) char kl1[TB];
+  __shared__ __attribute__((aligned(1024))) char vl1[TB];
+
+  uint32_t item = work_item(total, group_items);
+  const int sub = item % blocks_per_tile;
+  item /= blocks_per_tile;
+  const int qtile = item % g.ntiles;
+  item /= g.ntiles;
+  const int b = item % B;
+  const int head = ht.order[item / B];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 5, c32 = lane & 31;
+  const size_t seq = ((size_t)b * Hh + head) * (size_t)g.S;
+  const uint16_t* kb = k + seq * D;
+  const uint16_t* vb = v + seq * D;
+
+  const size_t row = seq + (size_t)qtile * g.L + sub * (NW * 32) + wave * 32 + c32;
+  bf16x8 qf[KS], dof[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = as_bf16x8(*(const u32x4*)(q + row * D + ks * 16 + grp * 8));
+    dof[ks] = as_bf16x8(*(const u32x4*)(dout + row * D + ks * 16 + grp * 8));
+  }
+  const float lrow = lse2[row], drow = dl[row];
+
+  const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
+  const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
+  const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
+            s2 = window_start(a2, w2, g.n2);
+  const int spt = g.L / kStage;
+  const int nst = w0 * w1 * w2 * spt;
+  int i0 = 0, i1 = 0, i2 = 0, jb = 0;
+  auto issue = [&](char* kl, char* vl) {
+    const int key0 = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L + jb * kStage;
+    if (++jb == spt) {
+      jb = 0;
+      if (++i2 == w2) {
+        i2 = 0;
+        if (++i1 == w1) {
+          i1 = 0;
+          ++i0;
+        }
+      }
+    }
+    dma_kv<D, kStage, NW>(kb, vb, (size_t)key0, kl, vl, wave, lane);
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  auto step = [&](const char* kl, const char* vl) {
+    bf16x8 kf[KS], vr[KS];
+    read_rows<D>(kl, kf, grp, c32);
+    read_rows<D>(vl, vr, grp, c32);
+    const f32x16 st = contract_rows<D>(kf, qf);   // S^T[key][q]
+    const f32x16 dpt = contract_rows<D>(vr, dof);  // dP^T[key][q]
+    bf16x8 ds[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * s + e], c_log2, -lrow));
+        ds[s][e] = (__bf16)(p * (dpt[8 * s + e] - drow));
+      }
+    bf16x8 ktf[DT][2];
+    read_cols<D>(kl, ktf, lane);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(ktf[dt][s], ds[s], acc[dt]);
+  };
+
+  issue(kl0, vl0);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < nst; j += 2) {
+    if (j + 1 < nst) issue(kl1, vl1);
+    step(kl0, vl0);
+    wait_dma();
+    __syncthreads();
+    if (j + 1 >= nst) break;
+    if (j + 2 < nst) issue(kl0, vl0);
+    step(kl1, vl1);
+    wait_dma();
+    __syncthreads();
+  }
+
+  // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj.
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 w;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(acc[dt][4 * i + jj] * scale);
+      *(bf16x4*)(dq + row * D + dt * 32 + 8 * i + 4 * grp) = w;
+    }
+}
+
+// --------------------------------------------------------------------------
+// 3. dK / dV (key-major).  Workgroup = NW waves x 32 key rows of one tile.
+// --------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void dma_stats(const float* __restrict__ lse2, const float* __restrict__ dl,
+                                          size_t row0, char* stat, int wave, int lane) {
+  // lanes 0-7 copy lse2[row0 .. row0+31], lanes 8-15 copy dl[...], into
+  // stat[0..127] and stat[128..255].
+  if (wave == 0 && lane < 16) {
+    const float* src = lane < 8 ? lse2 + row0 + lane * 4 : dl + row0 + (lane - 8) * 4;
+    dma16(src, stat);
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, Geometry g, HeadTable ht, int B, int Hh, float c_log2,
+    float scale, int blocks_per_tile, int total, int group_items) {
+  constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2;
+  __shared__ __attribute__((aligned(1024))) char ql0[TB];
+  __shared__ __attribute__((aligned(1024))) char dol0[TB];
+  __shared__ __attribute__((aligned(1024))) char ql1[TB];
+  __shared__ __attribute__((aligned(1024))) char dol1[TB];
+  __shared__ __attribute__((aligned(256))) char st0[256];
+  __shared__ __attribute__((aligned(256))) char st1[256];
+
+  uint32_t item = work_item(total, group_items);
+  const int sub = item % blocks_per_tile;
+  item /= blocks_per_tile;
+  const int ktile = item % g.ntiles;
+  item /= g.ntiles;
+  const int b = item % B;
+  const int head = ht.order[item / B];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 5, c32 = lane & 31;
+  const size_t seq = ((size_t)b * Hh + head) * (size_t)g.S;
+  const uint16_t* qb = q + seq * D;
+  const uint16_t* db = dout + seq * D;
+
+  // Resident key rows: K^T and V^T as B operands (lane holds 8 d of key c32).
+  const size_t krow0 = seq + (size_t)ktile * g.L + sub * (NW * 32) + wave * 32;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = as_bf16x8(*(const u32x4*)(k + (krow0 + c32) * D + ks * 16 + grp * 8));
+    vf[ks] = as_bf16x8(*(const u32x4*)(v + (krow0 + c32) * D + ks * 16 + grp * 8));
+  }
+
+  // Query tiles whose window holds this key tile: a box [lo, hi] per dimension.
+  const int a2 = ktile % g.n2, a1 = (ktile / g.n2) % g.n1, a0 = ktile / (g.n2 * g.n1);
+  int lo0, hi0, lo1, hi1, lo2, hi2;
+  window_transpose(a0, ht.wp[head][0], g.n0, &lo0, &hi0);
+  window_transpose(a1, ht.wp[head][1], g.n1, &lo1, &hi1);
+  window_transpose(a2, ht.wp[head][2], g.n2, &lo2, &hi2);
+  const int c0 = hi0 - lo0 + 1, c1 = hi1 - lo1 + 1, c2 = hi2 - lo2 + 1;
+  const int spt = g.L / kStage;
+  const int nst = c0 * c1 * c2 * spt;
+  int i0 = 0, i1 = 0, i2 = 0, jb = 0;
+  auto issue = [&](char* ql, char* dol, char* st) {
+    const size_t q0 =
+        (size_t)(((lo0 + i0) * g.n1 + (lo1 + i1)) * g.n2 + (lo2 + i2)) * g.L + jb * kStage;
+    if (++jb == spt) {
+      jb = 0;
+      if (++i2 == c2) {
+        i2 = 0;
+        if (++i1 == c1) {
+          i1 = 0;
+          ++i0;
+        }
+      }
+    }
+    dma_kv<D, kStage, NW>(qb, db, q0, ql, dol, wave, lane);
+    dma_stats<D>(lse2, dl, seq + q0, st, wave, lane);
+  };
+
+  f32x16 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dka[dt] = f32x16{};
+    dva[dt] = f32x16{};
+  }
+
+  auto step = [&](const char* ql, const char* dol, const char* st) {
+    bf16x8 qa[KS], da[KS];
+    read_rows<D>(ql, qa, grp, c32);
+    read_rows<D>(dol, da, grp, c32);
+    const f32x16 s = contract_rows<D>(qa, kf);   // S[q][key]
+    const f32x16 dp = contract_rows<D>(da, vf);  // dP[q][key]
+    // lane's queries: 8i + 4g + jj
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *(const f32x4*)(st + (8 * i + 4 * grp) * 4);
+      const f32x4 d4 = *(const f32x4*)(st + 128 + (8 * i + 4 * grp) * 4);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int e = 4 * i + jj;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj]));
+        pf[e >> 3][e & 7] = (__bf16)p;
+        dsf[e >> 3][e & 7] = (__bf16)(p * (dp[e] - d4[jj]));
+      }
+    }
+    bf16x8 dot[DT][2];
+    read_cols<D>(dol, dot, lane);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dva[dt] = mfma32(pf[ss], dot[dt][ss], dva[dt]);
+    bf16x8 qt[DT][2];
+    read_cols<D>(ql, qt, lane);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dka[dt] = mfma32(dsf[ss], qt[dt][ss], dka[dt]);
+  };
+
+  issue(ql0, dol0, st0);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < nst; j += 2) {
+    if (j + 1 < nst) issue(ql1, dol1, st1);
+    step(ql0, dol0, st0);
+    wait_dma();
+    __syncthreads();
+    if (j + 1 >= nst) break;
+    if (j + 2 < nst) issue(ql0, dol0, st0);
+    step(ql1, dol1, st1);
+    wait_dma();
+    __syncthreads();
+  }
+
+  // dK = scale * acc, dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32.
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const size_t r = krow0 + 8 * (e >> 2) + 4 * grp + (e & 3);
+      __bf16 kx = (__bf16)(dka[dt][e] * scale), vx = (__bf16)dva[dt][e];
+      dk[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, kx);
+      dv[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, vx);
+    }
+}
+
+inline int group_items_for(int seqs, int items_per_seq) {
+  for (int gsz = 1; gsz <= 8; ++gsz)
+    if ((gsz * items_per_seq) % 8 == 0 && seqs % gsz == 0) return gsz * items_per_seq;
+  return 0;
+}
+
+template <int D, int NW>
+hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                      const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk,
+                      uint16_t* dv, float* ws, const Geometry& g, const HeadTable& ht, int B,
+                      int Hh, float scale, hipStream_t st) {
+  const size_t rows = (size_t)B * Hh * g.S;
+  float* lse2 = ws;
+  float* dl = ws + rows;
+  const size_t threads = rows * (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
+                     st, o, dout, lse, lse2, dl, rows);
+  const int bpt = g.L / (NW * 32);
+  const int total = B * Hh * g.ntiles * bpt;
+  const int group = group_items_for(B * Hh, g.ntiles * bpt);
+  const float c_log2 = scale * kLog2e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
+                     dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k,
+                     v, dout, lse2, dl, dk, dv, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_bf16_supported(int D, int L) { return (D == 64 || D == 128) && L % 32 == 0; }
+
+hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* o, const uint16_t* dout, const float* lse,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, float* ws,
+                           const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
+                           float scale, hipStream_t st) {
+  const bool wide = g.L % 128 == 0;
+  if (D == 128)
+    return wide ? launch_bwd<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st)
+                : launch_bwd<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+  if (D == 64)
+    return wide ? launch_bwd<64, 4>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st)
+                : launch_bwd<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
   return hipErrorInvalidValue;
 }
 

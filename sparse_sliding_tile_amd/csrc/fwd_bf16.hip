@@ -47,35 +47,6 @@ struct FwdCfg {
   static constexpr int TILE_BYTES = KB * D * 2;
 };
 
-// K operand fragments of one 32-key stage: lane holds 8 d of key row c32.
-template <int D>
-__device__ __forceinline__ void read_k(const char* kl, bf16x8 (&kf)[D / 16], int grp, int c32) {
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    kf[ks] = as_bf16x8(lds_read16(kl, tile_off<D>(c32, ks * 2 + grp)));
-}
-
-// V^T operand fragments of one 32-key stage, read transposed from the
-// row-major V tile: lane i of each 16-lane group takes d = dt*32 + 16h + i and
-// keys (16s + 4g + r) and (16s + 8 + 4g + r), r = 0..3.
-template <int D>
-__device__ __forceinline__ void read_vt(const char* vl, bf16x8 (&vf)[D / 32][2], int lane) {
-  const int grp = lane >> 5, l16 = lane & 15, h = (lane >> 4) & 1;
-  const int vr = grp * 4 + (l16 >> 2);
-  const int vc = l16 & 3;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int d = dt * 32 + 16 * h + 4 * vc;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int r0 = 16 * s + vr;
-      const s16x4 lo = lds_read_tr(vl, tile_off<D>(r0, d >> 3) + (d & 4) * 2);
-      const s16x4 hi = lds_read_tr(vl, tile_off<D>(r0 + 8, d >> 3) + (d & 4) * 2);
-      vf[dt][s] = join_tr(lo, hi);
-    }
-  }
-}
-
 // S^T = K Q^T for one 32-key stage.
 template <int D, int QT>
 __device__ __forceinline__ void qk_stage(const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[QT][D / 16],
@@ -250,11 +221,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   wait_dma();
   __syncthreads();
   bf16x8 kf[C::KS];
-  read_k<D>(kl0, kf, grp, c32);
+  read_rows<D>(kl0, kf, grp, c32);
 
   auto stage = [&](int j, const char* vl_cur, const char* kl_nxt, char* kl_nn, char* vl_nn) {
     bf16x8 vf[C::DT][2];
-    read_vt<D>(vl_cur, vf, lane);
+    read_cols<D>(vl_cur, vf, lane);
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
     bf16x8 pf[QT][2];
@@ -263,7 +234,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       wait_dma();
       __syncthreads();
       if (j + 2 < nblk) issue(kl_nn, vl_nn);
-      read_k<D>(kl_nxt, kf, grp, c32);
+      read_rows<D>(kl_nxt, kf, grp, c32);
     }
     pv_stage<D, QT>(vf, pf, oacc);
   };

@@ -107,4 +107,36 @@ __device__ __forceinline__ void dma_kv(const uint16_t* __restrict__ kg, const ui
   }
 }
 
+// A/B operand fragments of a row-major [32 x D] tile (rows = keys or
+// queries): lane l holds 8 consecutive d of row l % 32 for each 16-wide k-step.
+template <int D>
+__device__ __forceinline__ void read_rows(const char* tl, bf16x8 (&f)[D / 16], int grp, int c32) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    f[ks] = as_bf16x8(lds_read16(tl, tile_off<D>(c32, ks * 2 + grp)));
+}
+
+// Transposed fragments of the same tile, [d][row] with the row order of the
+// 32x32 accumulator: lane i of each 16-lane group takes d = dt*32 + 16h + i
+// and rows (16s + 4g + r) and (16s + 8 + 4g + r), r = 0..3.  Element e of
+// fragment [dt][s] is row 16s + 8(e/4) + 4g + e%4, which is the row held in
+// element 8s + e of a 32x32 accumulator whose lane owns column l % 32.
+template <int D>
+__device__ __forceinline__ void read_cols(const char* tl, bf16x8 (&f)[D / 32][2], int lane) {
+  const int grp = lane >> 5, l16 = lane & 15, h = (lane >> 4) & 1;
+  const int vr = grp * 4 + (l16 >> 2);
+  const int vc = l16 & 3;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int d = dt * 32 + 16 * h + 4 * vc;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r0 = 16 * s + vr;
+      const s16x4 lo = lds_read_tr(tl, tile_off<D>(r0, d >> 3) + (d & 4) * 2);
+      const s16x4 hi = lds_read_tr(tl, tile_off<D>(r0 + 8, d >> 3) + (d & 4) * 2);
+      f[dt][s] = join_tr(lo, hi);
+    }
+  }
+}
+
 }  // namespace sta

@@ -388,6 +388,16 @@ def test_backward_key_rows_matches_full():
     np.testing.assert_allclose(dv2, dv[0, 0, rows], atol=1e-12)
 
 
+def test_backward_query_rows_matches_full():
+    latent, tile = (6, 16, 16), (2, 4, 4)
+    wins = [(1, 3, 3)]
+    q, k, v, do = (_rand((1, 1, 1536, 8), s) for s in (43, 44, 45, 46))
+    dq, _, _ = O.backward(q, k, v, do, latent, tile, wins, 0.3)
+    rows = np.array([0, 7, 31, 32, 900, 1535])
+    dq2 = O.backward_query_rows(q, k, v, do, latent, tile, wins[0], 0.3, 0, 0, rows)
+    np.testing.assert_allclose(dq2, dq[0, 0, rows], atol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def test_pins_catch_planted_window_mistake(monkeypatch):
