@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sliding Tile Attention hot path on one MI355X.
+
+One step = the whole forward path on one batch of the HunyuanVideo-shaped
+workload: tile reorder of Q, K, V (raster -> tile-major), sta_forward, tile
+unreorder of O, on latent (30, 48, 80), tile (6, 8, 8), 24 heads, head_dim 128,
+bf16, window (3, 3, 3) tiles for every head.  Inputs are seeded synthetic
+N(0, 1) tensors already resident in HBM when the timed region starts.
+
+value = counted forward FLOPs per step / step time, where counted FLOPs are
+4 * L^2 * D per computed (query tile, key tile) pair (Q K^T and P V only; no
+skipped pair, no softmax).  The JSON line also carries:
+  roofline      the sta_forward kernel alone, timed with events on its stream;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the workload;
+  legs          the dense attention kernel of the same build (speedup
+                denominator), the backward at the fine-tuning shape, the mixed
+                per-head window and Wan-shaped forwards, and reorder bandwidth.
+Everything runs on one GPU; --gpus above 1 is refused.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FWD_SRC = os.path.join(ROOT, "sparse_sliding_tile_amd", "csrc", "fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sta_forward_hunyuan_30x48x80_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-legs", action="store_true", help="time only the main forward step")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    return p.parse_args()
+
+
+def kh(window, n):
+    out = 1
+    for a, b in zip(window, n):
+        out *= min(a, b)
+    return out
+
+
+def fwd_flops(latent, tile, windows, batch, head_dim):
+    n = [a // b for a, b in zip(latent, tile)]
+    L = tile[0] * tile[1] * tile[2]
+    nt = n[0] * n[1] * n[2]
+    return sum(batch * nt * kh(w, n) * 4 * L * L * head_dim for w in windows)
+
+
+class Timer:
+    """Events on the current stream (the stream libsta launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.e0 = self.torch.cuda.Event(enable_timing=True)
+        self.e1 = self.torch.cuda.Event(enable_timing=True)
+        self.e0.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e1.record()
+        self.pairs.append((self.e0, self.e1))
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per sta_forward launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel source changed since."""
+    try:
+        vals = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
+        if vals.get("source_sha256_16") != source_hash(FWD_SRC):
+            return None
+        return float(vals["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, latent, tile, window, head_dim, target_s):
+    """The fp64 oracle, as it stands, on consecutive query tiles of head 0."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the machine's cores
+        threads = os.cpu_count()
+    n = [a // b for a, b in zip(latent, tile)]
+    L = tile[0] * tile[1] * tile[2]
+    q, k, v = (oracle.reorder(x[nm][:, :1].float().numpy().astype(np.float64), latent, tile)
+               for nm in ("q", "k", "v"))
+    done, t0 = 0, time.perf_counter()
+    while True:
+        rows = np.arange(done * L, (done + 1) * L)
+        oracle.forward(q, k, v, latent, tile, [window], head_dim ** -0.5, rows=rows)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= n[0] * n[1] * n[2]:
+            break
+    flops = done * kh(window, n) * 4 * L * L * head_dim
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} query tiles ({done * L} rows) of head 0 of 24, all {L * n[0] * n[1] * n[2]} keys "
+                      f"masked, fp64 numpy; {el:.1f} s; value counts the same 4*L^2*D per computed tile "
+                      f"pair as the GPU figure"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this build has no multi-GPU path; sharding by head is described in DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_sliding_tile_amd as sta
+    from sparse_sliding_tile_amd import inputs as I
+
+    sta.lib()
+    dev = torch.device("cuda:0")
+    name = "hunyuan_30x48x80_w333"
+    w = I.WORKLOADS[name]
+    latent, tile, wins, D, B, Hh = w["latent"], w["tile"], w["windows"], w["head_dim"], w["batch"], w["heads"]
+    S = latent[0] * latent[1] * latent[2]
+    log(f"[bench] generating {name} inputs")
+    x = I.workload_inputs(name)
+    q, k, v = (x[nm].to(dev) for nm in ("q", "k", "v"))
+    qt, kt, vt, ot = (torch.empty_like(q) for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hh, S), dtype=torch.float32, device=dev)
+    flops = fwd_flops(latent, tile, wins, B, D)
+    fwd_timer = Timer(torch)
+
+    def step(timed):
+        sta.tile_reorder(q, latent, tile, out=qt)
+        sta.tile_reorder(k, latent, tile, out=kt)
+        sta.tile_reorder(v, latent, tile, out=vt)
+        if timed:
+            with fwd_timer:
+                sta.forward(qt, kt, vt, latent, tile, wins, out=ot, lse=lse)
+        else:
+            sta.forward(qt, kt, vt, latent, tile, wins, out=ot, lse=lse)
+        sta.tile_unreorder(ot, latent, tile, out=o)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step(True)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    fwd_ms = fwd_timer.total_ms() / args.steps
+    log(f"[bench] step {ms_step:.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms), sta_forward {fwd_ms:.3f} ms")
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    result = {
+        "metric": "effective TFLOP/s and % bf16 MFMA peak, STA fwd at (30,48,80) latent",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "latent": list(latent), "tile": list(tile), "heads": Hh,
+                   "head_dim": D, "batch": B, "window": list(wins[0]),
+                   "step": "reorder q,k,v + sta_forward + unreorder o",
+                   "pct_of_peak_step": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "sta_forward (fwd_bf16_kernel)",
+                     "kernel_ms": round(fwd_ms, 4), "flops_per_launch": flops},
+    }
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(x, latent, tile, wins[0], D, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+
+    if not args.no_legs:
+        legs = {}
+        # dense denominator on the same tensors
+        dense_t = Timer(torch)
+        sta.dense_forward(qt, kt, vt, out=o, want_lse=False)
+        for _ in range(2):
+            with dense_t:
+                sta.dense_forward(qt, kt, vt, out=o, want_lse=False)
+        torch.cuda.synchronize()
+        dense_ms = dense_t.total_ms() / 2
+        dense_flops = B * Hh * 4 * S * S * D
+        legs["dense_forward"] = {"ms": round(dense_ms, 3), "tflops": round(dense_flops / dense_ms / 1e9, 1),
+                                 "speedup_sta_over_dense": round(dense_ms / fwd_ms, 2),
+                                 "ideal_speedup": round(dense_flops / flops, 2)}
+        # reorder bandwidth (one tensor: read + write)
+        rt = Timer(torch)
+        for _ in range(5):
+            with rt:
+                sta.tile_reorder(q, latent, tile, out=qt)
+        torch.cuda.synchronize()
+        r_ms = rt.total_ms() / 5
+        nbytes = 2 * q.numel() * q.element_size()
+        legs["tile_reorder"] = {"ms": round(r_ms, 4), "GB/s": round(nbytes / r_ms / 1e6, 1),
+                                "frac_of_hbm_peak": round(nbytes / r_ms / 1e6 / PEAK_HBM_GBS, 3)}
+        del x, q, k, v, qt, kt, vt, ot, o, lse
+        torch.cuda.empty_cache()
+        g = torch.Generator(device=dev).manual_seed(1)
+
+        def rand(shape):
+            return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        for lname in ("hunyuan_30x48x80_mixed", "wan_24x48x80_w335"):
+            lw = I.WORKLOADS[lname]
+            lS = lw["latent"][0] * lw["latent"][1] * lw["latent"][2]
+            shape = (lw["batch"], lw["heads"], lS, lw["head_dim"])
+            a, b_, c = rand(shape), rand(shape), rand(shape)
+            out = torch.empty_like(a)
+            ll = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+            t = Timer(torch)
+            sta.forward(a, b_, c, lw["latent"], lw["tile"], lw["windows"], out=out, lse=ll)
+            for _ in range(5):
+                with t:
+                    sta.forward(a, b_, c, lw["latent"], lw["tile"], lw["windows"], out=out, lse=ll)
+            torch.cuda.synchronize()
+            lms = t.total_ms() / 5
+            lf = fwd_flops(lw["latent"], lw["tile"], lw["windows"], lw["batch"], lw["head_dim"])
+            legs[lname] = {"ms": round(lms, 3), "tflops": round(lf / lms / 1e9, 1),
+                           "pct_of_peak": round(100 * lf / lms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+            if lname.endswith("mixed"):
+                legs[lname]["windows"] = [list(x_) for x_ in lw["windows"]]
+            del a, b_, c, out, ll
+        # backward at the fine-tuning shape
+        fw = I.WORKLOADS["finetune_24x64x64_w355"]
+        fS = fw["latent"][0] * fw["latent"][1] * fw["latent"][2]
+        shape = (fw["batch"], fw["heads"], fS, fw["head_dim"])
+        a, b_, c, do = rand(shape), rand(shape), rand(shape), rand(shape)
+        out, ll = sta.forward(a, b_, c, fw["latent"], fw["tile"], fw["windows"])
+        ws = torch.empty(sta.backward_workspace_bytes(shape[0], shape[1], shape[3], fw["latent"]),
+                         dtype=torch.uint8, device=dev)
+        t = Timer(torch)
+        sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)
+        for _ in range(3):
+            with t:
+                sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)
+        torch.cuda.synchronize()
+        bms = t.total_ms() / 3
+        bflops = fwd_flops(fw["latent"], fw["tile"], fw["windows"], fw["batch"], fw["head_dim"]) * 10 // 4
+        legs["finetune_24x64x64_w355_backward"] = {
+            "ms": round(bms, 3), "tflops": round(bflops / bms / 1e9, 1),
+            "pct_of_peak": round(100 * bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "counted": "10*L^2*D per tile pair (5 GEMMs); the kernels run 7 (deterministic dQ pass)"}
+        result["legs"] = legs
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -133,7 +133,7 @@ int sta_backward(const void* q, const void* k, const void* v, const void* o, con
 
 /* Dense softmax attention over all S keys: the full-attention baseline STA is
  * compared with ([STA-abs] compares with FlashAttention).  Same kernel family
- * and layout as sta_forward; S % 64 == 0 for STA_BF16. */
+ * and layout as sta_forward; S % 32 == 0 for STA_BF16. */
 int sta_dense_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                       int64_t Hh, int64_t S, int64_t D, float scale, sta_dtype dt, void* stream);
 

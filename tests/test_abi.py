@@ -1,0 +1,175 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/sta.h
+declares, rejects bad arguments with the documented codes before launching
+anything, and its host-side tile-pair list equals the oracle's bit for bit.
+
+Every call here fails validation (or is host-only), so no kernel is launched
+and no device memory is touched: the fake device pointers are never used.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import sparse_sliding_tile_amd._lib as L
+from sparse_sliding_tile_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sta.h")
+
+OK, ARG, NOT_MULT, WINDOW, UNSUP, ALIGN, HIP, WS, TOO_LARGE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+P = ctypes.c_void_p(0x10000)      # aligned stand-in, never dereferenced
+MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+NUL = ctypes.c_void_p(None)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|size_t|const char\*)\s+(sta_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, f"binding lacks {n}"
+
+
+def test_strerror_covers_codes(lib):
+    for c in (OK, ARG, NOT_MULT, WINDOW, UNSUP, ALIGN, HIP, WS, TOO_LARGE):
+        s = lib.sta_strerror(c).decode()
+        assert s and s != "unknown error code"
+    assert lib.sta_strerror(12345).decode() == "unknown error code"
+
+
+def d3(*a):
+    return L.Dim3(*a)
+
+
+def win(rows):
+    return np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=NUL, B=1, Hh=2, D=128, latent=(6, 16, 16), tile=(2, 4, 4),
+        windows=((3, 3, 3), (3, 3, 3)), scale=0.1, dt=L.STA_BF16):
+    w = win(windows)
+    return lib.sta_forward(q, k, v, o, lse, B, Hh, D, d3(*latent), d3(*tile), w.ctypes.data_as(ctypes.c_void_p),
+                           scale, dt, NUL)
+
+
+def test_forward_argument_errors(lib):
+    assert fwd(lib, q=NUL) == ARG
+    assert fwd(lib, o=NUL) == ARG
+    assert fwd(lib, scale=0.0) == ARG
+    assert fwd(lib, scale=-1.0) == ARG
+    assert fwd(lib, scale=float("nan")) == ARG
+    assert fwd(lib, B=0) == ARG
+    assert fwd(lib, latent=(5, 16, 16)) == NOT_MULT          # [STA-rebut]: whole tiles only
+    assert fwd(lib, latent=(29, 45, 76), tile=(6, 8, 8)) == NOT_MULT
+    assert fwd(lib, latent=(0, 16, 16)) == ARG
+    assert fwd(lib, windows=((3, 0, 3), (3, 3, 3))) == WINDOW
+    assert fwd(lib, windows=((3, 3, 3), (3, 3, -1))) == WINDOW
+    assert fwd(lib, D=96) == UNSUP                             # bf16 needs D in {64, 128}
+    assert fwd(lib, D=96, dt=L.STA_F32) == UNSUP
+    assert fwd(lib, dt=7) == UNSUP
+    assert fwd(lib, tile=(1, 4, 4), latent=(6, 16, 16)) == UNSUP   # L = 16 is not a multiple of 32
+    assert fwd(lib, q=MIS) == ALIGN
+    assert fwd(lib, lse=MIS) == ALIGN
+    many = [(3, 3, 3)] * 257
+    assert fwd(lib, Hh=257, windows=many) == UNSUP
+    assert lib.sta_forward(P, P, P, P, NUL, 1, 2, 128, d3(6, 16, 16), d3(2, 4, 4), NUL, 0.1, 0, NUL) == ARG
+
+
+def test_reorder_argument_errors(lib):
+    f = lib.sta_tile_reorder
+    assert f(NUL, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ARG
+    assert f(P, P, 1, 2, 64, d3(6, 16, 15), d3(2, 4, 4), 0, NUL) == NOT_MULT
+    assert f(MIS, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ALIGN
+    assert f(P, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 9, NUL) == UNSUP
+    assert lib.sta_tile_unreorder(P, NUL, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ARG
+    assert f(P, P, 1, 2, 0, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ARG
+
+
+def test_backward_argument_errors(lib):
+    w = win([(3, 3, 3)] * 2)
+    wp = w.ctypes.data_as(ctypes.c_void_p)
+    need = lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), 0)
+    assert need == 2 * 1 * 2 * 1536 * 4
+
+    def bwd(ws=P, nbytes=need, lse=P, dq=P, D=128, dt=0, windows=wp):
+        return lib.sta_backward(P, P, P, P, P, lse, dq, P, P, ws, nbytes, 1, 2, D, d3(6, 16, 16), d3(2, 4, 4),
+                                windows, 0.1, dt, NUL)
+    assert bwd(ws=NUL) == WS
+    assert bwd(nbytes=need - 1) == WS
+    assert bwd(lse=NUL) == ARG
+    assert bwd(dq=NUL) == ARG
+    assert bwd(dq=MIS) == ALIGN
+    assert bwd(D=80) == UNSUP
+    assert bwd(windows=NUL) == ARG
+
+
+def test_dense_argument_errors(lib):
+    f = lib.sta_dense_forward
+    assert f(P, P, P, P, NUL, 1, 2, 1000, 128, 0.1, 0, NUL) == UNSUP    # bf16 needs S % 32 == 0
+    assert f(P, P, P, P, NUL, 1, 2, 0, 128, 0.1, 0, NUL) == ARG
+    assert f(NUL, P, P, P, NUL, 1, 2, 1024, 128, 0.1, 0, NUL) == ARG
+    assert f(P, P, P, P, NUL, 1, 2, 1024, 128, 0.0, 0, NUL) == ARG
+
+
+def test_pairs_argument_errors(lib):
+    w = win([(3, 3, 3)])
+    wp = w.ctypes.data_as(ctypes.c_void_p)
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(4, 4, 4), wp, 1) == NOT_MULT
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), NUL, 1) == ARG
+    bad = win([(0, 3, 3)])
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), bad.ctypes.data_as(ctypes.c_void_p), 1) == WINDOW
+    assert lib.sta_tile_pairs(NUL, NUL, d3(6, 16, 16), d3(2, 4, 4), wp, 1, 0, NUL) == ARG
+
+
+PAIR_CASES = [((6, 16, 16), (2, 4, 4), [(3, 3, 3), (1, 2, 5)]),
+              ((30, 48, 80), (6, 8, 8), I.mixed_windows(24, 0)),
+              ((30, 48, 80), (6, 8, 8), [(3, 3, 3)] * 2),
+              ((24, 48, 80), (6, 8, 8), [(3, 3, 5)]),
+              ((24, 64, 64), (6, 8, 8), [(3, 5, 5)]),
+              ((5, 6, 10), (5, 3, 2), [(2, 2, 4), (9, 1, 1)]),
+              ((1, 8, 16), (1, 8, 8), [(1, 1, 1), (1, 1, 2)])]
+
+
+@pytest.mark.parametrize("latent,tile,wins", PAIR_CASES)
+def test_pair_count_matches_oracle(latent, tile, wins):
+    _, off = O.tile_pairs(latent, tile, wins)
+    assert L.tile_pairs_count(latent, tile, wins) == off[-1]
+
+
+@pytest.mark.parametrize("latent,tile,wins", PAIR_CASES)
+@pytest.mark.parametrize("transpose", [False, True])
+def test_host_pairs_bit_exact(latent, tile, wins, transpose):
+    p, off = L.tile_pairs_host(latent, tile, wins, transpose=transpose)
+    rp, roff = O.tile_pairs(latent, tile, wins, transpose=transpose)
+    assert np.array_equal(off, roff)
+    assert np.array_equal(p, rp)
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        L.lib()
+
+
+def test_product_never_imports_oracle():
+    pkg = os.path.join(ROOT, "sparse_sliding_tile_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), errors="replace").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
