@@ -68,6 +68,15 @@ __device__ __forceinline__ uint32_t work_item(int total, int group_items) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Wait for the oldest in-flight stage copy while up to two newer stages (each
+// PER copies per wave) stay in flight; `newer` is how many exist.
+template <int PER>
+__device__ __forceinline__ void wait_stage(int newer) {
+  if (newer >= 2) wait_dma_upto<2 * PER>();
+  else if (newer == 1) wait_dma_upto<PER>();
+  else wait_dma();
+}
+
 template <int D>
 __device__ __forceinline__ f32x16 contract_rows(const bf16x8 (&a)[D / 16], const bf16x8 (&b)[D / 16]) {
   f32x16 acc = f32x16{};
@@ -91,6 +100,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char vl0[TB];
   __shared__ __attribute__((aligned(1024))) char kl1[TB];
   __shared__ __attribute__((aligned(1024))) char vl1[TB];
+  __shared__ __attribute__((aligned(1024))) char kl2[TB];
+  __shared__ __attribute__((aligned(1024))) char vl2[TB];
+  __shared__ __attribute__((aligned(1024))) char kl3[TB];
+  __shared__ __attribute__((aligned(1024))) char vl3[TB];
 
   uint32_t item = work_item(total, group_items);
   const int sub = item % blocks_per_tile;
@@ -163,19 +176,31 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(ktf[dt][s], ds[s], acc[dt]);
   };
 
+  // Four-stage LDS ring: stage j sits in buffer j % 4; its copy is issued
+  // three stages ahead, right after the barrier that ends stage j - 4.
+  constexpr int PER = dma_kv_per_wave<D, kStage, NW>();
   issue(kl0, vl0);
-  wait_dma();
-  __syncthreads();
-  for (int j = 0; j < nst; j += 2) {
-    if (j + 1 < nst) issue(kl1, vl1);
-    step(kl0, vl0);
-    wait_dma();
-    __syncthreads();
+  if (nst > 1) issue(kl1, vl1);
+  if (nst > 2) issue(kl2, vl2);
+  if (nst > 3) issue(kl3, vl3);
+  wait_stage<PER>(nst - 1);
+  barrier_lds();
+  auto stage = [&](int j, const char* kl, const char* vl, char* kf_, char* vf_) {
+    step(kl, vl);
+    if (j + 1 < nst) {
+      wait_stage<PER>(nst - 2 - j);
+      barrier_lds();
+      if (j + 4 < nst) issue(kf_, vf_);
+    }
+  };
+  for (int j = 0; j < nst; j += 4) {
+    stage(j, kl0, vl0, kl0, vl0);
     if (j + 1 >= nst) break;
-    if (j + 2 < nst) issue(kl0, vl0);
-    step(kl1, vl1);
-    wait_dma();
-    __syncthreads();
+    stage(j + 1, kl1, vl1, kl1, vl1);
+    if (j + 2 >= nst) break;
+    stage(j + 2, kl2, vl2, kl2, vl2);
+    if (j + 3 >= nst) break;
+    stage(j + 3, kl3, vl3, kl3, vl3);
   }
 
   // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj.
@@ -204,8 +229,11 @@ __device__ __forceinline__ void dma_stats(const float* __restrict__ lse2, const 
   }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(
+// MODE 0 computes dV (S = Q K^T, P, dV += P^T dO); MODE 1 computes dK
+// (S, dP = dO V^T, dS, dK += dS^T Q).  Two launches instead of one keep the
+// resident state of each under the register file (one fused kernel spills).
+template <int D, int NW, int MODE, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dk,
@@ -233,13 +261,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(
   const uint16_t* qb = q + seq * D;
   const uint16_t* db = dout + seq * D;
 
-  // Resident key rows: K^T and V^T as B operands (lane holds 8 d of key c32).
+  // Resident key rows: K^T (and V^T for dK) as B operands (lane holds 8 d of key c32).
   const size_t krow0 = seq + (size_t)ktile * g.L + sub * (NW * 32) + wave * 32;
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 kf[KS], vf[MODE == 1 ? KS : 1];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = as_bf16x8(*(const u32x4*)(k + (krow0 + c32) * D + ks * 16 + grp * 8));
-    vf[ks] = as_bf16x8(*(const u32x4*)(v + (krow0 + c32) * D + ks * 16 + grp * 8));
+    if constexpr (MODE == 1)
+      vf[ks] = as_bf16x8(*(const u32x4*)(v + (krow0 + c32) * D + ks * 16 + grp * 8));
   }
 
   // Query tiles whose window holds this key tile: a box [lo, hi] per dimension.
@@ -269,71 +298,73 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(
     dma_stats<D>(lse2, dl, seq + q0, st, wave, lane);
   };
 
-  f32x16 dka[DT], dva[DT];
+  f32x16 acc[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dka[dt] = f32x16{};
-    dva[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
   auto step = [&](const char* ql, const char* dol, const char* st) {
-    bf16x8 qa[KS], da[KS];
-    read_rows<D>(ql, qa, grp, c32);
-    read_rows<D>(dol, da, grp, c32);
-    const f32x16 s = contract_rows<D>(qa, kf);   // S[q][key]
-    const f32x16 dp = contract_rows<D>(da, vf);  // dP[q][key]
-    // lane's queries: 8i + 4g + jj
-    bf16x8 pf[2], dsf[2];
+    f32x16 s, dp;
+    {
+      bf16x8 qa[KS];
+      read_rows<D>(ql, qa, grp, c32);
+      s = contract_rows<D>(qa, kf);   // S[q][key]
+    }
+    if constexpr (MODE == 1) {
+      bf16x8 da[KS];
+      read_rows<D>(dol, da, grp, c32);
+      dp = contract_rows<D>(da, vf);  // dP[q][key]
+    }
+    // lane's queries: 8i + 4g + jj; the A operand is P^T (MODE 0) or dS^T.
+    bf16x8 af[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *(const f32x4*)(st + (8 * i + 4 * grp) * 4);
-      const f32x4 d4 = *(const f32x4*)(st + 128 + (8 * i + 4 * grp) * 4);
+      f32x4 d4 = {};
+      if constexpr (MODE == 1) d4 = *(const f32x4*)(st + 128 + (8 * i + 4 * grp) * 4);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int e = 4 * i + jj;
         const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj]));
-        pf[e >> 3][e & 7] = (__bf16)p;
-        dsf[e >> 3][e & 7] = (__bf16)(p * (dp[e] - d4[jj]));
+        af[e >> 3][e & 7] = MODE == 0 ? (__bf16)p : (__bf16)(p * (dp[e] - d4[jj]));
       }
     }
-    bf16x8 dot[DT][2];
-    read_cols<D>(dol, dot, lane);
+    // B operand: dO^T (MODE 0) or Q^T, read transposed from the staged tile.
+    bf16x8 bt[DT][2];
+    read_cols<D>(MODE == 0 ? dol : ql, bt, lane);
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dva[dt] = mfma32(pf[ss], dot[dt][ss], dva[dt]);
-    bf16x8 qt[DT][2];
-    read_cols<D>(ql, qt, lane);
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dka[dt] = mfma32(dsf[ss], qt[dt][ss], dka[dt]);
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(af[ss], bt[dt][ss], acc[dt]);
   };
 
+  // Two-stage LDS ring: the copy of stage j + 1 is issued before stage j is
+  // computed.  Wave 0 also copies the stage statistics, so its waits cover one
+  // more copy than the other waves'.
   issue(ql0, dol0, st0);
   wait_dma();
-  __syncthreads();
+  barrier_lds();
   for (int j = 0; j < nst; j += 2) {
     if (j + 1 < nst) issue(ql1, dol1, st1);
     step(ql0, dol0, st0);
     wait_dma();
-    __syncthreads();
+    barrier_lds();
     if (j + 1 >= nst) break;
     if (j + 2 < nst) issue(ql0, dol0, st0);
     step(ql1, dol1, st1);
     wait_dma();
-    __syncthreads();
+    barrier_lds();
   }
 
-  // dK = scale * acc, dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32.
+  // dK = scale * acc or dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32.
+  uint16_t* out = MODE == 0 ? dv : dk;
+  const float osc = MODE == 0 ? 1.0f : scale;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const size_t r = krow0 + 8 * (e >> 2) + 4 * grp + (e & 3);
-      __bf16 kx = (__bf16)(dka[dt][e] * scale), vx = (__bf16)dva[dt][e];
-      dk[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, kx);
-      dv[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, vx);
+      const __bf16 x = (__bf16)(acc[dt][e] * osc);
+      out[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, x);
     }
 }
 
@@ -360,8 +391,10 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   const float c_log2 = scale * kLog2e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
                      dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k,
-                     v, dout, lse2, dl, dk, dv, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, 2>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
+                     k, v, dout, lse2, dl, dk, dv, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
+                     k, v, dout, lse2, dl, dk, dv, g, ht, B, Hh, c_log2, scale, bpt, total, group);
   return hipGetLastError();
 }
 

@@ -122,14 +122,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     HeadTable ht, int B, int Hh, float c_log2, int blocks_per_tile, int total, int group_items) {
   using C = FwdCfg<D, QT, NW>;
   constexpr int KB = C::KB;
-  // A ring of three stages, each buffer its own object so the compiler can
-  // tell the DMA target from the buffers being read.
+  // A ring of four stages, each buffer its own object so the compiler can
+  // tell the DMA targets from the buffers being read.
   __shared__ __attribute__((aligned(1024))) char kl0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vl0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kl1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vl1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kl2[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vl2[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kl3[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vl3[C::TILE_BYTES];
 
   // Work item.  Workgroups are dealt round-robin to the 8 XCDs (XCD x runs
   // every 8th blockIdx).  Items are ordered (head slot, batch, query tile,
@@ -211,19 +213,24 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     lrun[qt] = 0.f;
   }
 
-  // Pipeline: stage j sits in buffer j % 3.  While the MFMAs of stage j run,
-  // the V^T fragments of stage j (before Q K^T) and the K fragments of stage
-  // j + 1 (before P V) are read from LDS, and stage j + 2 is in flight from
-  // HBM.  The barrier between softmax and P V publishes stage j + 1 and frees
-  // buffer (j + 2) % 3, whose last reader was the P V of stage j - 1.
+  // Pipeline over 32-key stages; stage j sits in LDS buffer j % 4 and its
+  // HBM->LDS copy is issued two stages ahead.  In stage j: read the V^T
+  // fragments of j, Q K^T and softmax of j, then wait for the copy of stage
+  // j + 1 (leaving the copy of j + 2 in flight), barrier (all waves are past
+  // stage j - 1, so buffer (j + 3) % 4 is free), start the copy of j + 3, read
+  // the K fragments of j + 1 (they land during P V), and P V of j.
+  constexpr int PER = dma_kv_per_wave<D, KB, NW>();
+  static_assert(PER * NW == 2 * (KB / (1024 / (D * 2))), "copies must split evenly over waves");
   issue(kl0, vl0);
   if (nblk > 1) issue(kl1, vl1);
-  wait_dma();
-  __syncthreads();
+  if (nblk > 2) issue(kl2, vl2);
+  if (nblk > 2) wait_dma_upto<2 * PER>();
+  else wait_dma();
+  barrier_lds();
   bf16x8 kf[C::KS];
   read_rows<D>(kl0, kf, grp, c32);
 
-  auto stage = [&](int j, const char* vl_cur, const char* kl_nxt, char* kl_nn, char* vl_nn) {
+  auto stage = [&](int j, const char* vl_cur, const char* kl_nxt, char* kl_far, char* vl_far) {
     bf16x8 vf[C::DT][2];
     read_cols<D>(vl_cur, vf, lane);
     f32x16 sacc[QT];
@@ -231,19 +238,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     bf16x8 pf[QT][2];
     softmax_stage<D, QT>(sacc, pf, oacc, mrun, lrun, c_log2);
     if (j + 1 < nblk) {
-      wait_dma();
-      __syncthreads();
-      if (j + 2 < nblk) issue(kl_nn, vl_nn);
+      if (j + 2 < nblk) wait_dma_upto<PER>();
+      else wait_dma();
+      barrier_lds();
+      if (j + 3 < nblk) issue(kl_far, vl_far);
       read_rows<D>(kl_nxt, kf, grp, c32);
     }
     pv_stage<D, QT>(vf, pf, oacc);
   };
-  for (int j = 0; j < nblk; j += 3) {
-    stage(j, vl0, kl1, kl2, vl2);
+  for (int j = 0; j < nblk; j += 4) {
+    stage(j, vl0, kl1, kl3, vl3);
     if (j + 1 >= nblk) break;
     stage(j + 1, vl1, kl2, kl0, vl0);
     if (j + 2 >= nblk) break;
-    stage(j + 2, vl2, kl0, kl1, vl1);
+    stage(j + 2, vl2, kl3, kl1, vl1);
+    if (j + 3 >= nblk) break;
+    stage(j + 3, vl3, kl0, kl2, vl2);
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.

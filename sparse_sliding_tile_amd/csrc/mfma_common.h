@@ -71,6 +71,32 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
+// Wait until at most N vector-memory operations (here: DMA copies) of this
+// wave are still in flight (s_waitcnt vmcnt(N), expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_dma_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS pipelines.  The only LDS writes the kernels
+// make are DMA copies, each wave waits for its own with wait_dma*() first, so
+// the barrier needs no memory fence (__syncthreads() would also drain every
+// copy still in flight).  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// DMA instructions one wave issues for one dma_kv call (uniform over waves
+// when the segment count splits evenly).
+template <int D, int ROWS, int NW>
+constexpr int dma_kv_per_wave() {
+  return (2 * (ROWS / (1024 / (D * 2)))) / NW;
+}
+
 // x combined with the value of lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float xmax32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -92,6 +118,7 @@ __device__ __forceinline__ void dma_kv(const uint16_t* __restrict__ kg, const ui
   static_assert(ROWS % RPS == 0, "block rows must fill whole segments");
   constexpr int CPR = D / 8;                // chunks per row
   constexpr int PER = (2 * SEGS + NW - 1) / NW;
+  static_assert(PER < 64, "too many copies per wave");
   const int rin = lane / CPR;
   const int p = lane % CPR;
 #pragma unroll
