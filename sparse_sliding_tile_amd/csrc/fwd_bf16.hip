@@ -90,16 +90,20 @@ __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float mneg = -mrun[qt];
-    float ls = 0.f;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qt][8 * s + e], c_log2, mneg));
-        ls += p;
-        pf[qt][s][e] = (__bf16)p;
-      }
-    lrun[qt] += ls;
+      for (int e = 0; e < 8; ++e)
+        pf[qt][s][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][8 * s + e], c_log2, mneg));
+    // Row sum of the bf16 probabilities (the values P V uses), two per dot2.
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[qt][0][2 * e], pf[qt][0][2 * e + 1]}, one, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[qt][1][2 * e], pf[qt][1][2 * e + 1]}, one, ls1, false);
+    }
+    lrun[qt] += ls0 + ls1;
   }
 }
 
@@ -199,9 +203,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
     return key0;
   };
-  auto issue = [&](char* kl, char* vl) {
-    dma_kv<D, KB, NW>(kb, vb, (size_t)next_key0(), kl, vl, wave, lane);
-  };
+  const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
+  auto issue = [&](char* kl, char* vl) { copier.issue(kb, vb, (size_t)next_key0(), kl, vl); };
 
   f32x16 oacc[QT][C::DT];
   float mrun[QT], lrun[QT];
@@ -219,8 +222,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // j + 1 (leaving the copy of j + 2 in flight), barrier (all waves are past
   // stage j - 1, so buffer (j + 3) % 4 is free), start the copy of j + 3, read
   // the K fragments of j + 1 (they land during P V), and P V of j.
-  constexpr int PER = dma_kv_per_wave<D, KB, NW>();
-  static_assert(PER * NW == 2 * (KB / (1024 / (D * 2))), "copies must split evenly over waves");
+  constexpr int PER = KvDma<D, KB, NW>::PER;
   issue(kl0, vl0);
   if (nblk > 1) issue(kl1, vl1);
   if (nblk > 2) issue(kl2, vl2);

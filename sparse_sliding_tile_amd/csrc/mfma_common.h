@@ -134,6 +134,44 @@ __device__ __forceinline__ void dma_kv(const uint16_t* __restrict__ kg, const ui
   }
 }
 
+// The same copy with the per-lane parts worked out once: the source offset of
+// each lane's 16 bytes inside a block and the wave's LDS segments do not change
+// from block to block, so an issue costs one scalar base address per tensor
+// (the loads use the scalar-base + 32-bit lane-offset addressing form).  The
+// segments of each tile are dealt round-robin over the NW waves; wave_u must be
+// the wave index held uniformly (readfirstlane).
+template <int D, int ROWS, int NW>
+struct KvDma {
+  static constexpr int RPS = 1024 / (D * 2);  // rows per 1 KiB segment
+  static constexpr int SEGS = ROWS / RPS;     // segments per tile
+  static_assert(ROWS % RPS == 0 && SEGS % NW == 0, "segments must split evenly over waves");
+  static constexpr int PT = SEGS / NW;        // segments per wave per tile
+  static constexpr int PER = 2 * PT;          // copies per wave per issue
+  uint32_t goff[PT];
+  int wave_u;
+  __device__ __forceinline__ KvDma(int wave_uniform, int lane) : wave_u(wave_uniform) {
+    constexpr int CPR = D / 8;  // chunks per row
+    const int rin = lane / CPR, p = lane % CPR;
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+      const int r = (wave_u + e * NW) * RPS + rin;
+      goff[e] = (uint32_t)(r * D + ((p ^ (int)swz<D>(r)) * 8)) * 2u;
+    }
+  }
+  // Rows [row0, row0 + ROWS) of kg and vg into the tiles kl and vl.
+  __device__ __forceinline__ void issue(const uint16_t* kg, const uint16_t* vg, size_t row0, char* kl,
+                                        char* vl) const {
+    const char* kbase = (const char*)(kg + row0 * D);
+    const char* vbase = (const char*)(vg + row0 * D);
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+      const int seg = wave_u + e * NW;
+      dma16(kbase + goff[e], kl + seg * 1024);
+      dma16(vbase + goff[e], vl + seg * 1024);
+    }
+  }
+};
+
 // A/B operand fragments of a row-major [32 x D] tile (rows = keys or
 // queries): lane l holds 8 consecutive d of row l % 32 for each 16-wide k-step.
 template <int D>
