@@ -229,12 +229,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   if (nblk > 2) wait_dma_upto<2 * PER>();
   else wait_dma();
   barrier_lds();
-  bf16x8 kf[C::KS];
+  // A wave's LDS read issued after its own LDS copy waits for that copy to
+  // land, so each stage reads all its operands of the next stage first and
+  // only then starts the next copy.
+  bf16x8 kf[C::KS], vfa[C::DT][2], vfb[C::DT][2];
   read_rows<D>(kl0, kf, grp, c32);
+  read_cols<D>(vl0, vfa, lane);
 
-  auto stage = [&](int j, const char* vl_cur, const char* kl_nxt, char* kl_far, char* vl_far) {
-    bf16x8 vf[C::DT][2];
-    read_cols<D>(vl_cur, vf, lane);
+  auto stage = [&](int j, bf16x8 (&vf)[C::DT][2], bf16x8 (&vf_nxt)[C::DT][2], const char* kl_nxt,
+                   const char* vl_nxt, char* kl_far, char* vl_far) {
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
     bf16x8 pf[QT][2];
@@ -243,19 +246,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       if (j + 2 < nblk) wait_dma_upto<PER>();
       else wait_dma();
       barrier_lds();
-      if (j + 3 < nblk) issue(kl_far, vl_far);
       read_rows<D>(kl_nxt, kf, grp, c32);
+      read_cols<D>(vl_nxt, vf_nxt, lane);
+      asm volatile("" ::: "memory");
+      if (j + 3 < nblk) issue(kl_far, vl_far);
     }
     pv_stage<D, QT>(vf, pf, oacc);
   };
   for (int j = 0; j < nblk; j += 4) {
-    stage(j, vl0, kl1, kl3, vl3);
+    stage(j, vfa, vfb, kl1, vl1, kl3, vl3);
     if (j + 1 >= nblk) break;
-    stage(j + 1, vl1, kl2, kl0, vl0);
+    stage(j + 1, vfb, vfa, kl2, vl2, kl0, vl0);
     if (j + 2 >= nblk) break;
-    stage(j + 2, vl2, kl3, kl1, vl1);
+    stage(j + 2, vfa, vfb, kl3, vl3, kl1, vl1);
     if (j + 3 >= nblk) break;
-    stage(j + 3, vl3, kl0, kl2, vl2);
+    stage(j + 3, vfb, vfa, kl0, vl0, kl2, vl2);
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
