@@ -114,7 +114,9 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
                 float scale, sta_dtype dt, void* stream);
 
-/* Bytes of device workspace sta_backward needs (0 is a valid answer). */
+/* Bytes of device workspace sta_backward needs: 8*B*Hh*S for per-row
+ * statistics (fp32 Dl and LSE*log2(e)) plus, for STA_BF16, 4*Hh*(S/32) for a
+ * per-head order of the key tiles.  0 for non-positive sizes. */
 size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dtype dt);
 
 /* STA backward: the exact gradient of sta_forward (the pages name fine-tuning

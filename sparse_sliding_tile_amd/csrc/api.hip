@@ -200,10 +200,13 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
 size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
                                     sta_dtype dt) {
   (void)D;
-  (void)dt;
   if (B < 1 || Hh < 1 || latent.t < 1 || latent.h < 1 || latent.w < 1) return 0;
-  // Per query row: Dl = <dO, O> and LSE * log2(e), fp32.
-  return 2 * (size_t)B * Hh * latent.t * latent.h * latent.w * sizeof(float);
+  const size_t S = (size_t)latent.t * latent.h * latent.w;
+  // Per query row: Dl = <dO, O> and LSE * log2(e), fp32.  The bf16 path adds
+  // a key-tile order per head (int32); its tiles hold at least 32 tokens.
+  size_t bytes = 2 * (size_t)B * Hh * S * sizeof(float);
+  if (dt == STA_BF16) bytes += (size_t)Hh * (S / 32) * sizeof(int32_t);
+  return bytes;
 }
 
 int sta_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,

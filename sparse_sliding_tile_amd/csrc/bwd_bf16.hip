@@ -5,13 +5,18 @@
 // With P the window-masked softmax recomputed from the forward's LSE,
 //   Dl_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Dl_i),
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
-// Three launches, no atomics, deterministic:
+// Four launches, no atomics, deterministic:
+//   0. rank:  per head, the key tiles in order of decreasing work (the number
+//             of query tiles whose window holds them), for the key-major launch.
 //   1. prep:  Dl and LSE * log2(e) per query row, into the workspace.
 //   2. dQ:    query-tile-major, walking the window like the forward:
 //             S^T = K Q^T, dP^T = V dO^T (lane = query), dQ^T += K^T dS^T.
 //   3. dK/dV: key-tile-major, walking the query tiles whose window holds the
 //             key tile (an interval per dimension): S = Q K^T, dP = dO V^T
-//             (lane = key), dV += P^T dO, dK += dS^T Q.
+//             (lane = key), dV += P^T dO, dK += dS^T Q.  That count varies
+//             several-fold between edge and centre tiles, so workgroups are
+//             launched heaviest first (rank-major over all heads) and dealt
+//             round-robin to the XCDs, which keeps the tail of the launch short.
 // Every (query tile, key tile) pair is a full dense block, as in the forward.
 // The operand layouts, LDS swizzle and transposed reads are those of
 // mfma_common.h; a transposed read of a row-major [32 x D] tile gives the
@@ -54,6 +59,64 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
     dl[row] = s;
     lse2[row] = lse[row] * kLog2e;
   }
+}
+
+// --------------------------------------------------------------------------
+// 0. rank: tab[head][r] = the key tile of rank r for that head, ranks ordered
+//    by decreasing count of query tiles whose window holds the tile (ties by
+//    tile number).  One workgroup per head; with more than kRankTiles tiles the
+//    order is left as the identity.
+// --------------------------------------------------------------------------
+constexpr int kRankTiles = 8192;
+
+__global__ __launch_bounds__(256) void bwd_rank_kernel(Geometry g, HeadTable ht,
+                                                       int32_t* __restrict__ tab) {
+  __shared__ int cost[kRankTiles];
+  const int head = blockIdx.x, nt = g.ntiles;
+  int32_t* out = tab + (size_t)head * nt;
+  if (nt > kRankTiles) {
+    for (int i = threadIdx.x; i < nt; i += 256) out[i] = i;
+    return;
+  }
+  for (int i = threadIdx.x; i < nt; i += 256) {
+    const int a2 = i % g.n2, a1 = (i / g.n2) % g.n1, a0 = i / (g.n2 * g.n1);
+    int lo0, hi0, lo1, hi1, lo2, hi2;
+    window_transpose(a0, ht.wp[head][0], g.n0, &lo0, &hi0);
+    window_transpose(a1, ht.wp[head][1], g.n1, &lo1, &hi1);
+    window_transpose(a2, ht.wp[head][2], g.n2, &lo2, &hi2);
+    cost[i] = (hi0 - lo0 + 1) * (hi1 - lo1 + 1) * (hi2 - lo2 + 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nt; i += 256) {
+    const int ci = cost[i];
+    int r = 0;
+    for (int j = 0; j < nt; ++j) {
+      const int cj = cost[j];
+      r += (cj > ci) | ((cj == ci) & (j < i));
+    }
+    out[r] = i;
+  }
+}
+
+// Key-major work item: items are (rank, head slot, batch, sub-block), rank
+// slowest, so the heaviest key tiles of every head go first; consecutive
+// workgroups land on different XCDs (blockIdx round-robin).
+struct KeyItem {
+  int b, head, ktile, sub;
+};
+__device__ __forceinline__ KeyItem key_major_item(const int32_t* __restrict__ rank_tab, const Geometry& g,
+                                                  const HeadTable& ht, int B, int Hh,
+                                                  int blocks_per_tile) {
+  uint32_t item = blockIdx.x;
+  KeyItem it;
+  it.sub = item % blocks_per_tile;
+  item /= blocks_per_tile;
+  const uint32_t hb = item % (uint32_t)(B * Hh);
+  const int rank = item / (uint32_t)(B * Hh);
+  it.b = hb % B;
+  it.head = ht.order[hb / B];
+  it.ktile = rank_tab[(size_t)it.head * g.ntiles + rank];
+  return it;
 }
 
 // Work item decode shared by both kernels (see the forward for the XCD split).
@@ -237,8 +300,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, Geometry g, HeadTable ht, int B, int Hh, float c_log2,
-    float scale, int blocks_per_tile, int total, int group_items) {
+    uint16_t* __restrict__ dv, const int32_t* __restrict__ rank_tab, Geometry g, HeadTable ht,
+    int B, int Hh, float c_log2, float scale, int blocks_per_tile) {
   constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2;
   __shared__ __attribute__((aligned(1024))) char ql0[TB];
   __shared__ __attribute__((aligned(1024))) char dol0[TB];
@@ -247,13 +310,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   __shared__ __attribute__((aligned(256))) char st0[256];
   __shared__ __attribute__((aligned(256))) char st1[256];
 
-  uint32_t item = work_item(total, group_items);
-  const int sub = item % blocks_per_tile;
-  item /= blocks_per_tile;
-  const int ktile = item % g.ntiles;
-  item /= g.ntiles;
-  const int b = item % B;
-  const int head = ht.order[item / B];
+  const KeyItem it = key_major_item(rank_tab, g, ht, B, Hh, blocks_per_tile);
+  const int sub = it.sub, ktile = it.ktile, b = it.b, head = it.head;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 5, c32 = lane & 31;
@@ -382,6 +440,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   const size_t rows = (size_t)B * Hh * g.S;
   float* lse2 = ws;
   float* dl = ws + rows;
+  int32_t* rank_tab = (int32_t*)(ws + 2 * rows);
+  hipLaunchKernelGGL(bwd_rank_kernel, dim3((uint32_t)Hh), dim3(256), 0, st, g, ht, rank_tab);
   const size_t threads = rows * (D / 8);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
                      st, o, dout, lse, lse2, dl, rows);
@@ -392,9 +452,9 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
                      dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, 2>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
-                     k, v, dout, lse2, dl, dk, dv, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+                     k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
-                     k, v, dout, lse2, dl, dk, dv, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+                     k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
   return hipGetLastError();
 }
 

@@ -79,6 +79,9 @@ __device__ __forceinline__ void wait_dma_upto() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait for this wave's LDS accesses (s_waitcnt lgkmcnt(0), vmcnt untouched).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 // Workgroup barrier for the LDS pipelines.  The only LDS writes the kernels
 // make are DMA copies, each wave waits for its own with wait_dma*() first, so
 // the barrier needs no memory fence (__syncthreads() would also drain every

@@ -102,7 +102,8 @@ def test_backward_argument_errors(lib):
     w = win([(3, 3, 3)] * 2)
     wp = w.ctypes.data_as(ctypes.c_void_p)
     need = lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), 0)
-    assert need == 2 * 1 * 2 * 1536 * 4
+    assert need == 2 * 1 * 2 * 1536 * 4 + 2 * (1536 // 32) * 4   # row statistics + key-tile order
+    assert lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), 1) == 2 * 1 * 2 * 1536 * 4
 
     def bwd(ws=P, nbytes=need, lse=P, dq=P, D=128, dt=0, windows=wp):
         return lib.sta_backward(P, P, P, P, P, lse, dq, P, P, ws, nbytes, 1, 2, D, d3(6, 16, 16), d3(2, 4, 4),
