@@ -5,17 +5,17 @@
 // With P the window-masked softmax recomputed from the forward's LSE,
 //   Dl_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Dl_i),
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
-// Four launches, no atomics, deterministic:
+// Five launches, no atomics, deterministic:
 //   0. rank:  per head, the key tiles in order of decreasing work (the number
 //             of query tiles whose window holds them), for the key-major launch.
 //   1. prep:  Dl and LSE * log2(e) per query row, into the workspace.
 //   2. dQ:    query-tile-major, walking the window like the forward:
 //             S^T = K Q^T, dP^T = V dO^T (lane = query), dQ^T += K^T dS^T.
-//   3. dK/dV: key-tile-major, walking the query tiles whose window holds the
-//             key tile (an interval per dimension): S = Q K^T, dP = dO V^T
-//             (lane = key), dV += P^T dO, dK += dS^T Q.  That count varies
-//             several-fold between edge and centre tiles, so workgroups are
-//             launched heaviest first (rank-major over all heads) and dealt
+//   3. dV and 4. dK: key-tile-major, walking the query tiles whose window
+//             holds the key tile (an interval per dimension): S = Q K^T,
+//             dP = dO V^T (lane = key), dV += P^T dO, dK += dS^T Q.  That count
+//             varies several-fold between edge and centre tiles, so workgroups
+//             are launched heaviest first (rank-major over all heads) and dealt
 //             round-robin to the XCDs, which keeps the tail of the launch short.
 // Every (query tile, key tile) pair is a full dense block, as in the forward.
 // The operand layouts, LDS swizzle and transposed reads are those of
