@@ -241,7 +241,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
     bf16x8 pf[QT][2];
+    // Raised wave priority during the vector work: when the two waves of a
+    // SIMD compete for issue, the one in its softmax goes first and the
+    // other's matrix instructions fill the gaps (measured +2%).
+    __builtin_amdgcn_s_setprio(2);
     softmax_stage<D, QT>(sacc, pf, oacc, mrun, lrun, c_log2);
+    __builtin_amdgcn_s_setprio(0);
     if (j + 1 < nblk) {
       if (j + 2 < nblk) wait_dma_upto<PER>();
       else wait_dma();
