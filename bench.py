@@ -250,7 +250,7 @@ def main():
         def rand(shape):
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-        for lname in ("hunyuan_30x48x80_mixed", "wan_24x48x80_w335"):
+        for lname in ("hunyuan_30x48x80_mixed", "wan_24x48x80_w335", "image_2d_1x128x128_w155"):
             lw = I.WORKLOADS[lname]
             lS = lw["latent"][0] * lw["latent"][1] * lw["latent"][2]
             shape = (lw["batch"], lw["heads"], lS, lw["head_dim"])
@@ -270,26 +270,29 @@ def main():
             if lname.endswith("mixed"):
                 legs[lname]["windows"] = [list(x_) for x_ in lw["windows"]]
             del a, b_, c, out, ll
-        # backward at the fine-tuning shape
-        fw = I.WORKLOADS["finetune_24x64x64_w355"]
-        fS = fw["latent"][0] * fw["latent"][1] * fw["latent"][2]
-        shape = (fw["batch"], fw["heads"], fS, fw["head_dim"])
-        a, b_, c, do = rand(shape), rand(shape), rand(shape), rand(shape)
-        out, ll = sta.forward(a, b_, c, fw["latent"], fw["tile"], fw["windows"])
-        ws = torch.empty(sta.backward_workspace_bytes(shape[0], shape[1], shape[3], fw["latent"]),
-                         dtype=torch.uint8, device=dev)
-        t = Timer(torch)
-        sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)
-        for _ in range(3):
-            with t:
-                sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)
-        torch.cuda.synchronize()
-        bms = t.total_ms() / 3
-        bflops = fwd_flops(fw["latent"], fw["tile"], fw["windows"], fw["batch"], fw["head_dim"]) * 10 // 4
-        legs["finetune_24x64x64_w355_backward"] = {
-            "ms": round(bms, 3), "tflops": round(bflops / bms / 1e9, 1),
-            "pct_of_peak": round(100 * bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "counted": "10*L^2*D per tile pair (5 GEMMs); the kernels run 7 (deterministic dQ pass)"}
+        # backward at the fine-tuning shape, and at the HunyuanVideo shape with
+        # the mixed per-head windows
+        for bname, iters in (("finetune_24x64x64_w355", 3), ("hunyuan_30x48x80_mixed", 2)):
+            fw = I.WORKLOADS[bname]
+            fS = fw["latent"][0] * fw["latent"][1] * fw["latent"][2]
+            shape = (fw["batch"], fw["heads"], fS, fw["head_dim"])
+            a, b_, c, do = rand(shape), rand(shape), rand(shape), rand(shape)
+            out, ll = sta.forward(a, b_, c, fw["latent"], fw["tile"], fw["windows"])
+            ws = torch.empty(sta.backward_workspace_bytes(shape[0], shape[1], shape[3], fw["latent"]),
+                             dtype=torch.uint8, device=dev)
+            t = Timer(torch)
+            sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)
+            for _ in range(iters):
+                with t:
+                    sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)
+            torch.cuda.synchronize()
+            bms = t.total_ms() / iters
+            bflops = fwd_flops(fw["latent"], fw["tile"], fw["windows"], fw["batch"], fw["head_dim"]) * 10 // 4
+            legs[bname + "_backward"] = {
+                "ms": round(bms, 3), "tflops": round(bflops / bms / 1e9, 1),
+                "pct_of_peak": round(100 * bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                "counted": "10*L^2*D per tile pair (5 GEMMs); the kernels run 8 (dQ, dV and dK passes)"}
+            del a, b_, c, do, out, ll, ws
         result["legs"] = legs
 
     print(json.dumps(result), flush=True)

@@ -467,13 +467,18 @@ hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, float* ws,
                            const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
                            float scale, hipStream_t st) {
-  const bool wide = g.L % 128 == 0;
-  if (D == 128)
-    return wide ? launch_bwd<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st)
-                : launch_bwd<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
-  if (D == 64)
-    return wide ? launch_bwd<64, 4>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st)
-                : launch_bwd<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+  // Workgroups of 4, 2 or 1 waves (32 rows each), the widest the tile allows.
+  const int nw = g.L % 128 == 0 ? 4 : g.L % 64 == 0 ? 2 : 1;
+  if (D == 128) {
+    if (nw == 4) return launch_bwd<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+    if (nw == 2) return launch_bwd<128, 2>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+    return launch_bwd<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+  }
+  if (D == 64) {
+    if (nw == 4) return launch_bwd<64, 4>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+    if (nw == 2) return launch_bwd<64, 2>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+    return launch_bwd<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, ws, g, ht, B, Hh, scale, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -320,10 +320,12 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   const int L = g.L;
   if (D == 128) {
     if (L % 128 == 0) return launch_cfg<128, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    if (L % 64 == 0) return launch_cfg<128, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
     return launch_cfg<128, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
   }
   if (D == 64) {
     if (L % 128 == 0) return launch_cfg<64, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    if (L % 64 == 0) return launch_cfg<64, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
     return launch_cfg<64, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
   }
   return hipErrorInvalidValue;

@@ -30,6 +30,7 @@ BWD_SMALL = [  # latent, tile, B, windows, D
     ((6, 32, 32), (2, 8, 8), 2, [(3, 3, 3), (1, 4, 2)], 128),      # L = 128
     ((12, 16, 24), (6, 8, 8), 1, [(1, 3, 3), (2, 2, 2)], 128),     # L = 384
     ((6, 32, 32), (2, 8, 8), 1, [(3, 1, 3)], 64),
+    ((1, 32, 40), (1, 8, 8), 2, [(1, 3, 3), (1, 2, 4)], 128),     # 2D, L = 64
 ]
 
 
@@ -104,4 +105,45 @@ def test_backward_bf16_finetune_sampled(sta):
         for nm, got, r in (("dk", dk, rdk), ("dv", dv, rdv)):
             e = err_report(to64(got[0, h, kr]), r)
             print("head", h, nm, e)
+            assert e["max_abs"] < BF16_TOL and e["rel_rms"] < BF16_REL_RMS
+
+
+def test_backward_bf16_hunyuan_mixed_sampled(sta):
+    """HunyuanVideo shape (30,48,80) with the mixed per-head windows (full,
+    (1,6,10), (3,3,3), ...): dQ on sampled query rows of one head per window
+    kind, dK/dV on a corner key tile of a (3,3,3) head, and the full-size
+    invariants.  Exercises non-uniform transposed windows and the key-tile
+    ordering across heads of different weight."""
+    name = "hunyuan_30x48x80_mixed"
+    w = I.WORKLOADS[name]
+    latent, tile, wins, D = w["latent"], w["tile"], w["windows"], w["head_dim"]
+    n, L = O.tile_grid(latent, tile)
+    scale = D ** -0.5
+    x = I.workload_inputs(name, seed=2, with_do=True)
+    q, k, v, do = (_tm(sta, x[nm], latent, tile) for nm in ("q", "k", "v", "do"))
+    del x
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
+    dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
+    torch.cuda.synchronize()
+    dkf, dvf, dof = dk.float(), dv.float(), do.float()
+    assert bool((dkf.sum(2).abs() <= 2.0 ** -7 * dkf.abs().sum(2) + 1e-3).all())
+    assert bool(((dvf.sum(2) - dof.sum(2)).abs()
+                 <= 2.0 ** -7 * (dvf.abs().sum(2) + dof.abs().sum(2)) + 1e-3).all())
+    del dkf, dvf, dof
+    heads = sorted({wins.index(wd) for wd in set(wins)})   # one head of every window kind
+    qrows = np.r_[0:8, 150 * L - 8:150 * L + 8, (n[0] * n[1] * n[2] - 1) * L:(n[0] * n[1] * n[2] - 1) * L + 8]
+    krows = np.r_[0:8, L - 8:L]           # key tile 0
+    for h in heads:
+        hq, hk, hv, hdo = (to64(t[:, h:h + 1]) for t in (q, k, v, do))
+        rdq = O.backward_query_rows(hq, hk, hv, hdo, latent, tile, wins[h], scale, 0, 0, qrows)
+        e = err_report(to64(dq[0, h, torch.from_numpy(qrows).cuda()]), rdq)
+        print("head", h, wins[h], "dq", e)
+        assert e["max_abs"] < BF16_TOL and e["rel_rms"] < BF16_REL_RMS
+        if tuple(wins[h]) != (3, 3, 3):
+            continue   # the key-row oracle's cost grows with the window: one kind suffices
+        rdk, rdv = O.backward_key_rows(hq, hk, hv, hdo, latent, tile, wins[h], scale, 0, 0, krows)
+        kr = torch.from_numpy(krows).cuda()
+        for nm, got, r in (("dk", dk, rdk), ("dv", dv, rdv)):
+            e = err_report(to64(got[0, h, kr]), r)
+            print("head", h, wins[h], nm, e)
             assert e["max_abs"] < BF16_TOL and e["rel_rms"] < BF16_REL_RMS

@@ -125,6 +125,8 @@ BF16_SMALL = [  # latent, tile, B, windows, D   (tile volume 32 and 128; several
     ((6, 32, 32), (2, 8, 8), 2, [(3, 3, 3), (1, 1, 1), (3, 2, 4)], 128),
     ((12, 16, 24), (6, 8, 8), 1, [(1, 3, 3), (2, 2, 2)], 128),        # L = 384
     ((6, 32, 32), (2, 8, 8), 1, [(3, 3, 3), (1, 4, 2)], 64),
+    ((1, 32, 40), (1, 8, 8), 2, [(1, 3, 3), (1, 1, 5), (1, 9, 9)], 128),   # 2D, L = 64
+    ((1, 24, 40), (1, 8, 8), 1, [(1, 3, 3), (2, 2, 2)], 64),               # 2D, L = 64, D = 64
 ]
 
 
@@ -197,6 +199,10 @@ def test_forward_bf16_hunyuan_mixed_sampled(sta):
 
 def test_forward_bf16_wan_sampled(sta):
     _check_sampled(sta, "wan_24x48x80_w335", heads=[0, 39])
+
+
+def test_forward_bf16_image_2d_sampled(sta):
+    _check_sampled(sta, "image_2d_1x128x128_w155", heads=[0, 23])
 
 
 # ------------------------------------------------------------------ dense
