@@ -30,7 +30,12 @@ the pages are silent (each is listed in the design doc as well):
     so the window stays inside the tile grid; for even w' the extra tile falls
     on the low side);
   * windows are counted in tiles; a window < 1 is an error;
-  * the log-sum-exp uses the natural logarithm.
+  * the log-sum-exp uses the natural logarithm;
+  * a latent that is not a whole number of tiles is handled as [STA-rebut]'s
+    "padding with masking": it is padded up to the next tile multiple in each
+    dimension, windows live on the padded tile grid, padding tokens are never
+    keys, and the rows of padding tokens are outputs of no real token (O, LSE
+    and all gradients are zero there).
 Every function here is pinned by ``tests/test_oracle.py`` against brute force,
 closed forms, invariants and library routines.
 """
@@ -38,7 +43,8 @@ closed forms, invariants and library routines.
 import numpy as np
 
 __all__ = [
-    "tile_grid", "tile_major_index", "reorder", "unreorder", "window_start",
+    "tile_grid", "tile_major_index", "reorder", "unreorder", "padded_latent", "valid_positions",
+    "pad_reorder", "pad_unreorder", "window_start",
     "window_contains", "tile_pairs", "token_tile_coords", "window_mask",
     "forward", "backward", "backward_key_rows", "backward_query_rows", "dense_forward",
 ]
@@ -95,6 +101,64 @@ def unreorder(y, latent, tile):
     if y.shape[-2] != pi.size:
         raise ValueError("sequence axis does not match the latent")
     return y[..., pi, :].copy()
+
+
+def padded_latent(latent, tile):
+    """The smallest whole-tile latent holding ``latent``.
+
+    [STA-rebut], answer on input resolution, "padding with masking": a latent
+    such as (29, 45, 76) is padded to the tile-aligned (30, 48, 80) and the
+    padding tokens are masked out of the attention.
+    """
+    latent = tuple(int(v) for v in latent)
+    tile = tuple(int(v) for v in tile)
+    if len(latent) != 3 or len(tile) != 3 or min(latent) < 1 or min(tile) < 1:
+        raise ValueError("latent and tile are positive (T, H, W) triples")
+    return tuple(-(-a // b) * b for a, b in zip(latent, tile))
+
+
+def _raster_in_padded(latent, tile):
+    """Raster index inside the padded latent of every raster token of ``latent``."""
+    T, H, W = (int(v) for v in latent)
+    _, P1, P2 = padded_latent(latent, tile)
+    tau, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    return ((tau * P1 + y) * P2 + x).reshape(-1).astype(np.int64)
+
+
+def valid_positions(latent, tile, order="tile"):
+    """Boolean [S_pad]: the position of the padded latent holds a real token.
+
+    ``order`` is the order of the padded sequence: "tile" (tile-major) or
+    "raster".  All true when the latent is a whole number of tiles.
+    """
+    P = padded_latent(latent, tile)
+    v = np.zeros(P[0] * P[1] * P[2], dtype=bool)
+    v[_raster_in_padded(latent, tile)] = True
+    if order == "raster":
+        return v
+    if order != "tile":
+        raise ValueError("order is 'tile' or 'raster'")
+    out = np.empty_like(v)
+    out[tile_major_index(P, tile)] = v
+    return out
+
+
+def pad_reorder(x, latent, tile):
+    """Raster tokens of ``latent`` (axis -2) -> tile-major sequence of the
+    padded latent; rows of padding tokens are zero."""
+    P = padded_latent(latent, tile)
+    idx = _raster_in_padded(latent, tile)
+    if x.shape[-2] != idx.size:
+        raise ValueError("sequence axis does not match the latent")
+    xp = np.zeros(x.shape[:-2] + (P[0] * P[1] * P[2], x.shape[-1]), dtype=x.dtype)
+    xp[..., idx, :] = x
+    return reorder(xp, P, tile)
+
+
+def pad_unreorder(y, latent, tile):
+    """Inverse of ``pad_reorder``: the raster tokens of ``latent`` (crop)."""
+    P = padded_latent(latent, tile)
+    return unreorder(y, P, tile)[..., _raster_in_padded(latent, tile), :].copy()
 
 
 def window_start(q, w, n):
@@ -204,6 +268,7 @@ def forward(q, k, v, latent, tile, windows, scale, order="tile", rows=None, chun
     then has shape [B, Hh, len(rows), D].
     """
     windows = _check_qkv(q, k, v, windows)
+    grid, valid = _padding(latent, tile, order)
     B, Hh, S, D = q.shape
     rows = np.arange(S) if rows is None else np.asarray(rows)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
@@ -212,7 +277,9 @@ def forward(q, k, v, latent, tile, windows, scale, order="tile", rows=None, chun
     for h in range(Hh):
         for c0 in range(0, rows.size, chunk):
             r = rows[c0:c0 + chunk]
-            m = window_mask(latent, tile, windows[h], order, rows=r)
+            m = window_mask(grid, tile, windows[h], order, rows=r)
+            if valid is not None:
+                m &= valid[None, :]
             for b in range(B):
                 s = scale * (q[b, h, r] @ k[b, h].T)
                 s[~m] = -np.inf
@@ -221,7 +288,21 @@ def forward(q, k, v, latent, tile, windows, scale, order="tile", rows=None, chun
                 l = e.sum(axis=1, keepdims=True)
                 o[b, h, c0:c0 + r.size] = (e @ v[b, h]) / l
                 lse[b, h, c0:c0 + r.size] = (mx + np.log(l))[:, 0]
+    if valid is not None:
+        o[:, :, ~valid[rows]] = 0.0
+        lse[:, :, ~valid[rows]] = 0.0
     return o, lse
+
+
+def _padding(latent, tile, order):
+    """The whole-tile grid latent to build windows on, and the key validity
+    mask over it (None when the latent is already a whole number of tiles)."""
+    grid = padded_latent(latent, tile)
+    if grid == tuple(int(v) for v in latent):
+        return grid, None
+    if order != "tile":
+        raise ValueError("a padded latent is only defined in tile-major order")
+    return grid, valid_positions(latent, tile)
 
 
 def backward(q, k, v, do, latent, tile, windows, scale, order="tile"):
@@ -234,16 +315,21 @@ def backward(q, k, v, do, latent, tile, windows, scale, order="tile"):
     dV = P^T dO.  Meant for small grids (it forms the S x S matrices).
     """
     windows = _check_qkv(q, k, v, windows)
+    grid, valid = _padding(latent, tile, order)
     B, Hh, S, D = q.shape
     q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for h in range(Hh):
-        m = window_mask(latent, tile, windows[h], order)
+        m = window_mask(grid, tile, windows[h], order)
+        if valid is not None:
+            m &= valid[None, :]
         for b in range(B):
             s = scale * (q[b, h] @ k[b, h].T)
             s[~m] = -np.inf
             p = np.exp(s - s.max(axis=1, keepdims=True))
             p /= p.sum(axis=1, keepdims=True)
+            if valid is not None:
+                p[~valid] = 0.0     # rows of padding tokens belong to no real query
             o = p @ v[b, h]
             dl = (do[b, h] * o).sum(axis=1, keepdims=True)
             dp = do[b, h] @ v[b, h].T
@@ -263,14 +349,18 @@ def backward_key_rows(q, k, v, do, latent, tile, win, scale, b, h, key_rows, ord
     dS give dK_j = scale sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i.
     """
     key_rows = np.asarray(key_rows)
+    grid, valid = _padding(latent, tile, order)
     qf, kf, vf, dof = (np.asarray(a[b, h], dtype=np.float64) for a in (q, k, v, do))
-    S = qf.shape[0]
-    qi = np.nonzero(window_mask(latent, tile, win, order, cols=key_rows).any(axis=1))[0]
+    qi = np.nonzero(window_mask(grid, tile, win, order, cols=key_rows).any(axis=1))[0]
+    if valid is not None:
+        qi = qi[valid[qi]]              # padding rows are no query
     dk = np.zeros((key_rows.size, qf.shape[1]))
     dv = np.zeros_like(dk)
     for c0 in range(0, qi.size, 512):
         r = qi[c0:c0 + 512]
-        m = window_mask(latent, tile, win, order, rows=r)
+        m = window_mask(grid, tile, win, order, rows=r)
+        if valid is not None:
+            m &= valid[None, :]
         s = scale * (qf[r] @ kf.T)
         s[~m] = -np.inf
         p = np.exp(s - s.max(axis=1, keepdims=True))
@@ -281,6 +371,9 @@ def backward_key_rows(q, k, v, do, latent, tile, win, scale, b, h, key_rows, ord
         ds = pj * (dof[r] @ vf[key_rows].T - dl)
         dk += scale * (ds.T @ qf[r])
         dv += pj.T @ dof[r]
+    if valid is not None:
+        dk[~valid[key_rows]] = 0.0
+        dv[~valid[key_rows]] = 0.0
     return dk, dv
 
 
@@ -292,11 +385,14 @@ def backward_query_rows(q, k, v, do, latent, tile, win, scale, b, h, rows, order
     dS_ij = P_ij (<dO_i, v_j> - Dl_i) and dQ_i = scale sum_j dS_ij k_j.
     """
     rows = np.asarray(rows)
+    grid, valid = _padding(latent, tile, order)
     qf, kf, vf, dof = (np.asarray(a[b, h], dtype=np.float64) for a in (q, k, v, do))
     out = np.zeros((rows.size, qf.shape[1]))
     for c0 in range(0, rows.size, 256):
         r = rows[c0:c0 + 256]
-        m = window_mask(latent, tile, win, order, rows=r)
+        m = window_mask(grid, tile, win, order, rows=r)
+        if valid is not None:
+            m &= valid[None, :]
         s = scale * (qf[r] @ kf.T)
         s[~m] = -np.inf
         p = np.exp(s - s.max(axis=1, keepdims=True))
@@ -305,6 +401,8 @@ def backward_query_rows(q, k, v, do, latent, tile, win, scale, b, h, rows, order
         dl = (dof[r] * o).sum(axis=1, keepdims=True)
         ds = p * (dof[r] @ vf.T - dl)
         out[c0:c0 + r.size] = scale * (ds @ kf)
+    if valid is not None:
+        out[~valid[rows]] = 0.0
     return out
 
 

@@ -430,3 +430,143 @@ def test_pins_catch_planted_mask_mistake(monkeypatch):
     monkeypatch.setattr(O.sta_oracle, "window_mask", truncated)
     bad, _ = O.sta_oracle.forward(q, k, v, latent, tile, [(3, 3, 3)], 0.5, order="raster")
     assert np.abs(bad - good).max() > 1e-3
+
+
+# ---------------------------------------------------------------- padding with masking
+
+PAD_LATENT, PAD_TILE = (3, 5, 6), (2, 2, 4)     # padded to (4, 6, 8): tile grid 2x3x2, 90 real of 192
+
+
+def test_padded_latent_and_valid_positions():
+    assert O.padded_latent((29, 45, 76), (6, 8, 8)) == (30, 48, 80)    # the pages' example
+    assert O.padded_latent((30, 48, 80), (6, 8, 8)) == (30, 48, 80)
+    v = O.valid_positions(PAD_LATENT, PAD_TILE)
+    assert v.size == 4 * 6 * 8 and v.sum() == 3 * 5 * 6
+    # tile-major: position a*L + i holds a real token iff its padded coordinates are inside
+    L = 2 * 2 * 4
+    for pos in range(v.size):
+        a, i = divmod(pos, L)
+        a0, a1, a2 = a // 6, (a // 2) % 3, a % 2
+        i0, i1, i2 = i // 8, (i // 4) % 2, i % 4
+        tau, y, x = a0 * 2 + i0, a1 * 2 + i1, a2 * 4 + i2
+        assert v[pos] == (tau < 3 and y < 5 and x < 6)
+    assert O.valid_positions((4, 6, 8), PAD_TILE).all()
+
+
+def test_pad_reorder_brute_force_and_round_trip():
+    T, H, W = PAD_LATENT
+    x = _rand((2, T * H * W, 3), 60)
+    y = O.pad_reorder(x, PAD_LATENT, PAD_TILE)
+    assert y.shape == (2, 192, 3)
+    for tau in range(T):
+        for yy in range(H):
+            for xx in range(W):
+                a = ((tau // 2) * 3 + yy // 2) * 2 + xx // 4
+                i = ((tau % 2) * 2 + yy % 2) * 4 + xx % 4
+                assert np.array_equal(y[:, a * 16 + i], x[:, (tau * H + yy) * W + xx])
+    assert not y[:, ~O.valid_positions(PAD_LATENT, PAD_TILE)].any()    # padding rows are zero
+    assert np.array_equal(O.pad_unreorder(y, PAD_LATENT, PAD_TILE), x)
+    # a whole-tile latent: the same as the plain reorder
+    z = _rand((1, 192, 2), 61)
+    assert np.array_equal(O.pad_reorder(z, (4, 6, 8), PAD_TILE), O.reorder(z, (4, 6, 8), PAD_TILE))
+
+
+def _brute_force_padded(q, k, v, latent, tile, wins, scale):
+    """Raster tokens of a latent that is not a whole number of tiles: the tile
+    grid is the padded one (ceil), windows slide on it, and only real tokens
+    are keys.  Scalar loops and math.exp."""
+    T, H, W = latent
+    t, h, w = tile
+    n = (-(-T // t), -(-H // h), -(-W // w))
+    B, Hh, S, D = q.shape
+    coords = [(tau, y, x) for tau in range(T) for y in range(H) for x in range(W)]
+    tc = [(tau // t, y // h, x // w) for tau, y, x in coords]
+    out = np.zeros_like(q)
+    lse = np.zeros((B, Hh, S))
+    for hh in range(Hh):
+        wins_d = [[_window_by_sliding(qq, wins[hh][d], n[d]) for qq in range(n[d])] for d in range(3)]
+        for b in range(B):
+            for i in range(S):
+                vis = [j for j in range(S) if all(tc[j][d] in wins_d[d][tc[i][d]] for d in range(3))]
+                s = [scale * sum(q[b, hh, i, c] * k[b, hh, j, c] for c in range(D)) for j in vis]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                tot = sum(e)
+                for c in range(D):
+                    out[b, hh, i, c] = sum(e[a] * v[b, hh, j, c] for a, j in enumerate(vis)) / tot
+                lse[b, hh, i] = mx + math.log(tot)
+    return out, lse
+
+
+def test_padded_forward_matches_brute_force():
+    wins = [(1, 2, 1), (2, 3, 2), (1, 1, 2)]
+    S = 90
+    q, k, v = (_rand((1, 3, S, 5), s) for s in (62, 63, 64))
+    ref_o, ref_l = _brute_force_padded(q, k, v, PAD_LATENT, PAD_TILE, wins, 0.6)
+    qt, kt, vt = (O.pad_reorder(a, PAD_LATENT, PAD_TILE) for a in (q, k, v))
+    o, l = O.forward(qt, kt, vt, PAD_LATENT, PAD_TILE, wins, 0.6)
+    np.testing.assert_allclose(O.pad_unreorder(o, PAD_LATENT, PAD_TILE), ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.pad_unreorder(l[..., None], PAD_LATENT, PAD_TILE)[..., 0], ref_l,
+                               rtol=0, atol=1e-12)
+    pad = ~O.valid_positions(PAD_LATENT, PAD_TILE)
+    assert not o[:, :, pad].any() and not l[:, :, pad].any()
+
+
+def test_padded_forward_ignores_padding_values():
+    """Whatever the padding rows hold, no real row changes."""
+    wins = [(2, 2, 2)]
+    q, k, v = (_rand((1, 1, 90, 4), s) for s in (65, 66, 67))
+    qt, kt, vt = (O.pad_reorder(a, PAD_LATENT, PAD_TILE) for a in (q, k, v))
+    o, l = O.forward(qt, kt, vt, PAD_LATENT, PAD_TILE, wins, 0.5)
+    pad = ~O.valid_positions(PAD_LATENT, PAD_TILE)
+    for a in (qt, kt, vt):
+        a[:, :, pad] = 7.0
+    o2, l2 = O.forward(qt, kt, vt, PAD_LATENT, PAD_TILE, wins, 0.5)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(l2, l)
+
+
+def test_padded_full_window_is_dense_over_real_tokens():
+    """A window covering the padded grid: attention over every real token."""
+    latent, tile = (29, 5, 7), (6, 2, 4)
+    S = 29 * 5 * 7
+    q, k, v = (_rand((1, 2, S, 8), s) for s in (68, 69, 70))
+    qt, kt, vt = (O.pad_reorder(a, latent, tile) for a in (q, k, v))
+    o, l = O.forward(qt, kt, vt, latent, tile, [(9, 9, 9), (5, 3, 2)], 0.35)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(a) for a in (q, k, v)), scale=0.35).numpy()
+    np.testing.assert_allclose(O.pad_unreorder(o, latent, tile), ref, rtol=0, atol=1e-12)
+    lse_ref = torch.logsumexp(0.35 * torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2), -1).numpy()
+    np.testing.assert_allclose(O.pad_unreorder(l[..., None], latent, tile)[..., 0], lse_ref, rtol=0, atol=1e-12)
+
+
+def test_padded_backward_matches_autograd():
+    """Autograd through SDPA over the real tokens (raster order) with the mask
+    of the padded tile grid built by the test's own sliding-window rule."""
+    latent, tile, wins, scale = PAD_LATENT, PAD_TILE, [(1, 2, 1), (2, 3, 2)], 0.45
+    T, H, W = latent
+    n = (2, 3, 2)
+    coords = [(tau // 2, y // 2, x // 4) for tau in range(T) for y in range(H) for x in range(W)]
+    masks = []
+    for win in wins:
+        wd = [[_window_by_sliding(qq, win[d], n[d]) for qq in range(n[d])] for d in range(3)]
+        masks.append([[all(cj[d] in wd[d][ci[d]] for d in range(3)) for cj in coords] for ci in coords])
+    q, k, v, do = (_rand((2, 2, 90, 6), s) for s in (71, 72, 73, 74))
+    qt, kt, vt = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.tensor(masks)[None], scale=scale)
+    out.backward(torch.from_numpy(do))
+    ref = (qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy())
+    args = [O.pad_reorder(a, latent, tile) for a in (q, k, v, do)]
+    got = O.backward(*args, latent, tile, wins, scale)
+    pad = ~O.valid_positions(latent, tile)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(O.pad_unreorder(g, latent, tile), r, rtol=0, atol=1e-11)
+        assert not g[:, :, pad].any()
+    # the sampled-row helpers agree with the whole-tensor gradients
+    rows = np.arange(192)
+    dq_rows = O.backward_query_rows(*args, latent, tile, wins[1], scale, 1, 1, rows)
+    np.testing.assert_allclose(dq_rows, got[0][1, 1], rtol=0, atol=1e-12)
+    dk_rows, dv_rows = O.backward_key_rows(*args, latent, tile, wins[1], scale, 1, 1, rows)
+    np.testing.assert_allclose(dk_rows, got[1][1, 1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv_rows, got[2][1, 1], rtol=0, atol=1e-12)
