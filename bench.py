@@ -56,7 +56,7 @@ def kh(window, n):
 
 
 def fwd_flops(latent, tile, windows, batch, head_dim):
-    n = [a // b for a, b in zip(latent, tile)]
+    n = [-(-a // b) for a, b in zip(latent, tile)]   # tile grid (padded latents: ceil)
     L = tile[0] * tile[1] * tile[2]
     nt = n[0] * n[1] * n[2]
     return sum(batch * nt * kh(w, n) * 4 * L * L * head_dim for w in windows)
@@ -250,9 +250,10 @@ def main():
         def rand(shape):
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-        for lname in ("hunyuan_30x48x80_mixed", "wan_24x48x80_w335", "image_2d_1x128x128_w155"):
+        for lname in ("hunyuan_30x48x80_mixed", "wan_24x48x80_w335", "image_2d_1x128x128_w155",
+                      "hunyuan_29x45x76_w333_padded"):
             lw = I.WORKLOADS[lname]
-            lS = lw["latent"][0] * lw["latent"][1] * lw["latent"][2]
+            lS = sta.tile_major_len(lw["latent"], lw["tile"])
             shape = (lw["batch"], lw["heads"], lS, lw["head_dim"])
             a, b_, c = rand(shape), rand(shape), rand(shape)
             out = torch.empty_like(a)
@@ -274,11 +275,11 @@ def main():
         # the mixed per-head windows
         for bname, iters in (("finetune_24x64x64_w355", 3), ("hunyuan_30x48x80_mixed", 2)):
             fw = I.WORKLOADS[bname]
-            fS = fw["latent"][0] * fw["latent"][1] * fw["latent"][2]
+            fS = sta.tile_major_len(fw["latent"], fw["tile"])
             shape = (fw["batch"], fw["heads"], fS, fw["head_dim"])
             a, b_, c, do = rand(shape), rand(shape), rand(shape), rand(shape)
             out, ll = sta.forward(a, b_, c, fw["latent"], fw["tile"], fw["windows"])
-            ws = torch.empty(sta.backward_workspace_bytes(shape[0], shape[1], shape[3], fw["latent"]),
+            ws = torch.empty(sta.backward_workspace_bytes(shape[0], shape[1], shape[3], fw["latent"], fw["tile"]),
                              dtype=torch.uint8, device=dev)
             t = Timer(torch)
             sta.backward(a, b_, c, out, do, ll, fw["latent"], fw["tile"], fw["windows"], workspace=ws)

@@ -13,16 +13,24 @@
  *               has its own window size.
  *   [STA-rebut] "Fast Video Generation with Sliding Tile Attention", OpenReview
  *               rebuttal, answer on input resolution: tile (6,8,8); the latent
- *               must be an integer multiple of the tile.
+ *               should be an integer multiple of the tile, and other latents are
+ *               handled by padding with masking.
  *
  * Conventions shared by every entry point
  *   - Shapes are (T, H, W) triples, W fastest.  A raster token r = (tau*H+y)*W+x.
- *   - Tensors are contiguous [B, Hh, S, D] (D innermost), S = T*H*W, element type
- *     bf16 (STA_BF16) or fp32 (STA_F32, the fp32 debug instance).  LSE is fp32
- *     [B, Hh, S] in the same token order as the tensors it belongs to.
+ *   - Tensors are contiguous [B, Hh, S, D] (D innermost), element type bf16
+ *     (STA_BF16) or fp32 (STA_F32, the fp32 debug instance).  Raster-order
+ *     tensors have S = T*H*W rows; tile-major tensors have S' = n0*n1*n2*L rows.
+ *     LSE is fp32 [B, Hh, S'] in tile-major order.
  *   - Tile-major order: tiles in raster order over the tile grid
- *     n = (T/t, H/h, W/w), tokens in raster order inside a tile; tile number a
- *     occupies sequence positions [a*L, (a+1)*L), L = t*h*w.
+ *     n = (ceil(T/t), ceil(H/h), ceil(W/w)), tokens in raster order inside a
+ *     tile; tile number a occupies sequence positions [a*L, (a+1)*L), L = t*h*w.
+ *   - Padding with masking [STA-rebut]: when the latent is not a whole number of
+ *     tiles, the tile grid covers the latent padded up to whole tiles (S' > S).
+ *     Tile-major positions whose (t, h, w) coordinate lies outside the latent
+ *     are padding: they are never keys, and O, LSE, dQ, dK and dV are written as
+ *     zero there.  Their contents in q, k, v and dout must be finite
+ *     (sta_tile_reorder writes zeros); they affect no other row.
  *   - Window of a head: (wt, wh, ww) in tiles, each >= 1.  Along a dimension with
  *     n tiles, w' = min(w, n) and the window of query tile q covers tiles
  *     [s, s + w') with s = clamp(q - floor(w'/2), 0, n - w'): the centre is
@@ -57,7 +65,7 @@ typedef enum { STA_BF16 = 0, STA_F32 = 1 } sta_dtype;
 enum {
   STA_OK = 0,
   STA_ERR_ARG = -1,               /* null pointer, non-positive size, bad scale */
-  STA_ERR_NOT_TILE_MULTIPLE = -2, /* latent not a whole number of tiles [STA-rebut] */
+  STA_ERR_NOT_TILE_MULTIPLE = -2, /* unused since padding with masking is supported */
   STA_ERR_WINDOW = -3,            /* a window entry < 1 */
   STA_ERR_UNSUPPORTED = -4,       /* head_dim, tile volume or dtype not built */
   STA_ERR_ALIGN = -5,             /* a tensor pointer not 16-byte aligned */
@@ -73,12 +81,14 @@ const char* sta_strerror(int code);
 
 /* Tile reorder [STA-meth], raster -> tile-major along S:
  *   y[b, hh, pi(r), :] = x[b, hh, r, :]
- * where pi(r) is the tile-major position of raster token r.  x and y are
- * distinct [B, Hh, S, D] buffers of type dt.  A bit-exact copy. */
+ * where pi(r) is the tile-major position of raster token r.  x is
+ * [B, Hh, S, D], y is [B, Hh, S', D] (S' = S for a whole-tile latent), distinct
+ * buffers of type dt.  A bit-exact copy; padding rows of y are set to zero. */
 int sta_tile_reorder(const void* x, void* y, int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
                      sta_dim3 tile, sta_dtype dt, void* stream);
 
-/* Inverse of sta_tile_reorder: x[b, hh, r, :] = y[b, hh, pi(r), :]. */
+/* Inverse of sta_tile_reorder: x[b, hh, r, :] = y[b, hh, pi(r), :] for the S
+ * raster tokens (padding rows of y are not read). */
 int sta_tile_unreorder(const void* y, void* x, int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
                        sta_dim3 tile, sta_dtype dt, void* stream);
 
@@ -106,18 +116,19 @@ int sta_tile_pairs_host(int32_t* pairs_host, int64_t* head_offsets_host, sta_dim
 /* STA forward [STA-abs]: for every (b, hh) and query position i of query tile a,
  *   O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j   over key positions j whose
  *   tile lies in the window of a,   LSE_i = ln sum_j exp(scale * <q_i, k_j>).
- * q, k, v, o: [B, Hh, S, D] in TILE-MAJOR order (see sta_tile_reorder).
- * lse: fp32 [B, Hh, S] or NULL.  scale > 0 (usually 1/sqrt(D)).
+ * q, k, v, o: [B, Hh, S', D] in TILE-MAJOR order (see sta_tile_reorder).
+ * lse: fp32 [B, Hh, S'] or NULL.  scale > 0 (usually 1/sqrt(D)).
  * STA_BF16: bf16 in/out, fp32 accumulation, MFMA; needs D in {64, 128} and
  * L % 32 == 0.  STA_F32: fp32 in/out, fp32 arithmetic; needs D <= 128. */
 int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                 int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
                 float scale, sta_dtype dt, void* stream);
 
-/* Bytes of device workspace sta_backward needs: 8*B*Hh*S for per-row
- * statistics (fp32 Dl and LSE*log2(e)) plus, for STA_BF16, 4*Hh*(S/32) for a
- * per-head order of the key tiles.  0 for non-positive sizes. */
-size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dtype dt);
+/* Bytes of device workspace sta_backward needs: 8*B*Hh*S' for per-row
+ * statistics (fp32 Dl and LSE*log2(e)) plus, for STA_BF16, 4*Hh*n0*n1*n2 for a
+ * per-head order of the key tiles.  0 for invalid sizes. */
+size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
+                                    sta_dim3 tile, sta_dtype dt);
 
 /* STA backward: the exact gradient of sta_forward (the pages name fine-tuning
  * with STA [STA-meth], which needs it).  With P the window-masked softmax,

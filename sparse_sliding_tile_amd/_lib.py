@@ -34,7 +34,7 @@ SIGNATURES = {
     "sta_tile_pairs_host": (ctypes.c_int, [c_vp, c_vp, Dim3, Dim3, c_vp, c_i64, ctypes.c_int]),
     "sta_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
                                    c_f32, ctypes.c_int, c_vp]),
-    "sta_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, Dim3, ctypes.c_int]),
+    "sta_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int]),
     "sta_backward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                     c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
     "sta_dense_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
@@ -114,19 +114,49 @@ def _shape4(x, name):
     return x.shape
 
 
+def raster_len(latent):
+    """Tokens of the latent (rows of a raster-order tensor)."""
+    t, h, w = (int(a) for a in latent)
+    return t * h * w
+
+
+def tile_major_len(latent, tile):
+    """Rows of a tile-major tensor: the latent padded up to whole tiles."""
+    return int(np.prod([-(-int(a) // int(b)) * int(b) for a, b in zip(latent, tile)]))
+
+
+def _same(ref, name, *tensors):
+    for n, t in tensors:
+        if tuple(t.shape) != tuple(ref) or t.dtype != tensors[0][1].dtype:
+            raise ValueError(f"{n} must match {name}: shape {tuple(ref)}, dtype {tensors[0][1].dtype}")
+
+
 def tile_reorder(x, latent, tile, out=None):
-    """Raster -> tile-major along S of a [B, Hh, S, D] tensor."""
+    """Raster [B, Hh, T*H*W, D] -> tile-major [B, Hh, S', D] (S' padded up to
+    whole tiles; padding rows are zero)."""
     B, Hh, S, D = _shape4(x, "x")
-    out = torch.empty_like(x) if out is None else out
+    if S != raster_len(latent):
+        raise ValueError(f"x has {S} rows, the latent {latent} has {raster_len(latent)} tokens")
+    shape = (B, Hh, tile_major_len(latent, tile), D)
+    out = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    _same(shape, "the tile-major shape", ("out", out))
+    if out.dtype != x.dtype:
+        raise ValueError("out must have the dtype of x")
     _check(lib().sta_tile_reorder(_dev(x, "x"), _dev(out, "out"), B, Hh, D, _dim3(latent), _dim3(tile),
                                   _dtype(x), _stream(x)), "sta_tile_reorder")
     return out
 
 
 def tile_unreorder(y, latent, tile, out=None):
-    """Tile-major -> raster along S of a [B, Hh, S, D] tensor."""
+    """Tile-major [B, Hh, S', D] -> raster [B, Hh, T*H*W, D] (padding dropped)."""
     B, Hh, S, D = _shape4(y, "y")
-    out = torch.empty_like(y) if out is None else out
+    if S != tile_major_len(latent, tile):
+        raise ValueError(f"y has {S} rows, tile-major {latent}/{tile} has {tile_major_len(latent, tile)}")
+    shape = (B, Hh, raster_len(latent), D)
+    out = torch.empty(shape, dtype=y.dtype, device=y.device) if out is None else out
+    _same(shape, "the raster shape", ("out", out))
+    if out.dtype != y.dtype:
+        raise ValueError("out must have the dtype of y")
     _check(lib().sta_tile_unreorder(_dev(y, "y"), _dev(out, "out"), B, Hh, D, _dim3(latent), _dim3(tile),
                                     _dtype(y), _stream(y)), "sta_tile_unreorder")
     return out
@@ -167,11 +197,16 @@ def tile_pairs_host(latent, tile, windows, transpose=False):
 def forward(q, k, v, latent, tile, windows, scale=None, out=None, lse=None, want_lse=True):
     """STA forward on tile-major [B, Hh, S, D] tensors: returns (O, LSE or None)."""
     B, Hh, S, D = _shape4(q, "q")
+    if S != tile_major_len(latent, tile):
+        raise ValueError(f"q has {S} rows, tile-major {latent}/{tile} has {tile_major_len(latent, tile)}")
     scale = float(D) ** -0.5 if scale is None else float(scale)
     w = _windows(windows, Hh)
     out = torch.empty_like(q) if out is None else out
+    _same(q.shape, "q", ("q", q), ("k", k), ("v", v), ("out", out))
     if lse is None and want_lse:
         lse = torch.empty((B, Hh, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, Hh, S) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, Hh, S]")
     lp = _dev(lse, "lse") if lse is not None else c_vp(None)
     _check(lib().sta_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, D,
                              _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale, _dtype(q),
@@ -179,17 +214,22 @@ def forward(q, k, v, latent, tile, windows, scale=None, out=None, lse=None, want
     return out, lse
 
 
-def backward_workspace_bytes(B, Hh, D, latent, dtype=torch.bfloat16):
+def backward_workspace_bytes(B, Hh, D, latent, tile, dtype=torch.bfloat16):
     dt = STA_BF16 if dtype == torch.bfloat16 else STA_F32
-    return int(lib().sta_backward_workspace_bytes(B, Hh, D, _dim3(latent), dt))
+    return int(lib().sta_backward_workspace_bytes(B, Hh, D, _dim3(latent), _dim3(tile), dt))
 
 
 def backward(q, k, v, o, do, lse, latent, tile, windows, scale=None, workspace=None):
     """STA backward on tile-major tensors: returns (dQ, dK, dV)."""
     B, Hh, S, D = _shape4(q, "q")
+    if S != tile_major_len(latent, tile):
+        raise ValueError(f"q has {S} rows, tile-major {latent}/{tile} has {tile_major_len(latent, tile)}")
+    _same(q.shape, "q", ("q", q), ("k", k), ("v", v), ("o", o), ("do", do))
+    if tuple(lse.shape) != (B, Hh, S) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hh, S]")
     scale = float(D) ** -0.5 if scale is None else float(scale)
     w = _windows(windows, Hh)
-    nbytes = backward_workspace_bytes(B, Hh, D, latent, q.dtype)
+    nbytes = backward_workspace_bytes(B, Hh, D, latent, tile, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -206,6 +246,7 @@ def dense_forward(q, k, v, scale=None, out=None, want_lse=True):
     B, Hh, S, D = _shape4(q, "q")
     scale = float(D) ** -0.5 if scale is None else float(scale)
     out = torch.empty_like(q) if out is None else out
+    _same(q.shape, "q", ("q", q), ("k", k), ("v", v), ("out", out))
     lse = torch.empty((B, Hh, S), dtype=torch.float32, device=q.device) if want_lse else None
     lp = _dev(lse, "lse") if lse is not None else c_vp(None)
     _check(lib().sta_dense_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, S, D,

@@ -23,21 +23,27 @@ bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 int make_geometry(sta_dim3 latent, sta_dim3 tile, Geometry* g) {
   if (latent.t < 1 || latent.h < 1 || latent.w < 1 || tile.t < 1 || tile.h < 1 || tile.w < 1)
     return STA_ERR_ARG;
-  if (latent.t % tile.t || latent.h % tile.h || latent.w % tile.w) return STA_ERR_NOT_TILE_MULTIPLE;
-  const int64_t S = (int64_t)latent.t * latent.h * latent.w;
-  if (S >= (1ll << 31)) return STA_ERR_TOO_LARGE;
+  // A latent that is not a whole number of tiles is padded up (ceil grid).
+  const int64_t n0 = (latent.t + (int64_t)tile.t - 1) / tile.t;
+  const int64_t n1 = (latent.h + (int64_t)tile.h - 1) / tile.h;
+  const int64_t n2 = (latent.w + (int64_t)tile.w - 1) / tile.w;
+  const int64_t L = (int64_t)tile.t * tile.h * tile.w;
+  const int64_t S = n0 * n1 * n2 * L;
+  if (L >= (1ll << 31) || S >= (1ll << 31)) return STA_ERR_TOO_LARGE;
   g->T = latent.t;
   g->H = latent.h;
   g->W = latent.w;
   g->t = tile.t;
   g->h = tile.h;
   g->w = tile.w;
-  g->n0 = latent.t / tile.t;
-  g->n1 = latent.h / tile.h;
-  g->n2 = latent.w / tile.w;
-  g->L = tile.t * tile.h * tile.w;
+  g->n0 = (int)n0;
+  g->n1 = (int)n1;
+  g->n2 = (int)n2;
+  g->L = (int)L;
   g->S = (int)S;
+  g->Sr = latent.t * latent.h * latent.w;
   g->ntiles = g->n0 * g->n1 * g->n2;
+  g->padded = (latent.t % tile.t || latent.h % tile.h || latent.w % tile.w) ? 1 : 0;
   return STA_OK;
 }
 
@@ -198,14 +204,15 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
 }
 
 size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
-                                    sta_dtype dt) {
+                                    sta_dim3 tile, sta_dtype dt) {
   (void)D;
-  if (B < 1 || Hh < 1 || latent.t < 1 || latent.h < 1 || latent.w < 1) return 0;
-  const size_t S = (size_t)latent.t * latent.h * latent.w;
-  // Per query row: Dl = <dO, O> and LSE * log2(e), fp32.  The bf16 path adds
-  // a key-tile order per head (int32); its tiles hold at least 32 tokens.
+  Geometry g;
+  if (B < 1 || Hh < 1 || make_geometry(latent, tile, &g) != STA_OK) return 0;
+  const size_t S = (size_t)g.S;
+  // Per tile-major row: Dl = <dO, O> and LSE * log2(e), fp32.  The bf16 path
+  // adds a key-tile order per head (int32).
   size_t bytes = 2 * (size_t)B * Hh * S * sizeof(float);
-  if (dt == STA_BF16) bytes += (size_t)Hh * (S / 32) * sizeof(int32_t);
+  if (dt == STA_BF16) bytes += (size_t)Hh * g.ntiles * sizeof(int32_t);
   return bytes;
 }
 
@@ -221,7 +228,7 @@ int sta_backward(const void* q, const void* k, const void* v, const void* o, con
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return STA_ERR_ARG;
   if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
   if ((st = check_sizes(B, Hh, D, g))) return st;
-  if (!workspace || ws_bytes < sta_backward_workspace_bytes(B, Hh, D, latent, dt))
+  if (!workspace || ws_bytes < sta_backward_workspace_bytes(B, Hh, D, latent, tile, dt))
     return STA_ERR_WORKSPACE;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
   for (const void* p : ptrs)

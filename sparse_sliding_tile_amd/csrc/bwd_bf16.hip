@@ -217,11 +217,36 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
+  // Padded latents: keys at padding positions of a partial key tile get
+  // P = 0 (a second walk over the key blocks, for the stage being computed).
+  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  auto mask_keys = [&](f32x16& st) {
+    if (!g.padded) return;
+    const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
+    if (tile_partial(k0, k1, k2, g)) {
+      const uint32_t bits = block_real_bits(k0, k1, k2, cjb * kStage, g, lane);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!elem_real(bits, e)) st[e] = -INFINITY;
+    }
+    if (++cjb == spt) {
+      cjb = 0;
+      if (++ci2 == w2) {
+        ci2 = 0;
+        if (++ci1 == w1) {
+          ci1 = 0;
+          ++ci0;
+        }
+      }
+    }
+  };
+
   auto step = [&](const char* kl, const char* vl) {
     bf16x8 kf[KS], vr[KS];
     read_rows<D>(kl, kf, grp, c32);
     read_rows<D>(vl, vr, grp, c32);
-    const f32x16 st = contract_rows<D>(kf, qf);   // S^T[key][q]
+    f32x16 st = contract_rows<D>(kf, qf);         // S^T[key][q]
+    mask_keys(st);
     const f32x16 dpt = contract_rows<D>(vr, dof);  // dP^T[key][q]
     bf16x8 ds[2];
 #pragma unroll
@@ -266,14 +291,17 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
     stage(j + 3, kl3, vl3, kl3, vl3);
   }
 
-  // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj.
+  // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj; zero
+  // on padding rows.
+  const int rin = sub * (NW * 32) + wave * 32 + c32;  // row inside the query tile
+  const float osc = (!g.padded || token_real(a0, a1, a2, rin, g)) ? scale : 0.0f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x4 w;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(acc[dt][4 * i + jj] * scale);
+      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(acc[dt][4 * i + jj] * osc);
       *(bf16x4*)(dq + row * D + dt * 32 + 8 * i + 4 * grp) = w;
     }
 }
@@ -360,7 +388,30 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
+  // Padded latents: padding rows of a partial query tile are no query; their
+  // P (and dS) is zero.  A second walk over the query blocks, for the stage
+  // being computed; returns the real-row bits (all set when nothing is masked).
+  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  auto query_bits = [&]() -> uint32_t {
+    uint32_t bits = 0xffffffffu;
+    if (!g.padded) return bits;
+    const int q0 = lo0 + ci0, q1 = lo1 + ci1, q2 = lo2 + ci2;
+    if (tile_partial(q0, q1, q2, g)) bits = block_real_bits(q0, q1, q2, cjb * kStage, g, lane);
+    if (++cjb == spt) {
+      cjb = 0;
+      if (++ci2 == c2) {
+        ci2 = 0;
+        if (++ci1 == c1) {
+          ci1 = 0;
+          ++ci0;
+        }
+      }
+    }
+    return bits;
+  };
+
   auto step = [&](const char* ql, const char* dol, const char* st) {
+    const uint32_t qbits = query_bits();
     f32x16 s, dp;
     {
       bf16x8 qa[KS];
@@ -382,7 +433,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int e = 4 * i + jj;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj]));
+        const float p = elem_real(qbits, e) ? __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj])) : 0.0f;
         af[e >> 3][e & 7] = MODE == 0 ? (__bf16)p : (__bf16)(p * (dp[e] - d4[jj]));
       }
     }
@@ -413,15 +464,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     barrier_lds();
   }
 
-  // dK = scale * acc or dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32.
+  // dK = scale * acc or dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32;
+  // zero on padding rows.
   uint16_t* out = MODE == 0 ? dv : dk;
   const float osc = MODE == 0 ? 1.0f : scale;
+  const uint32_t kbits = g.padded ? block_real_bits(a0, a1, a2, sub * (NW * 32) + wave * 32, g, lane)
+                                  : 0xffffffffu;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const size_t r = krow0 + 8 * (e >> 2) + 4 * grp + (e & 3);
-      const __bf16 x = (__bf16)(acc[dt][e] * osc);
+      const __bf16 x = (__bf16)(elem_real(kbits, e) ? acc[dt][e] * osc : 0.0f);
       out[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, x);
     }
 }

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   for (int i0 = 0; i0 < w0; ++i0)
     for (int i1 = 0; i1 < w1; ++i1)
       for (int i2 = 0; i2 < w2; ++i2) {
-        const int kt = ((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2);
+        const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
+        const int kt = (k0 * g.n1 + k1) * g.n2 + k2;
         for (int j0 = 0; j0 < g.L; j0 += kChunk) {
           const int nk = min(kChunk, g.L - j0);
           __syncthreads();
@@ -73,7 +74,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
           for (int j = 0; j < kChunk; ++j) {
             float dot = 0.f;
             for (int d = 0; d < D; ++d) dot = fmaf(qv[d], ks[j][d], dot);
-            s[j] = j < nk ? dot * scale : -INFINITY;
+            const bool key = j < nk && (!g.padded || token_real(k0, k1, k2, j0 + j, g));
+            s[j] = key ? dot * scale : -INFINITY;
             mc = fmaxf(mc, s[j]);
           }
           const float mn = fmaxf(m, mc);
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
           l *= corr;
           for (int d = 0; d < D; ++d) acc[d] *= corr;
           for (int j = 0; j < nk; ++j) {
-            const float p = expf(s[j] - mn);
+            const float p = expf(s[j] - mn);  // 0 for a masked key
             l += p;
             for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[j][d], acc[d]);
           }
@@ -89,9 +91,11 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
         }
       }
   if (!active) return;
-  const float inv = 1.f / l;
+  // Padding rows (padded latents) are no query: zero output.
+  const bool real = !g.padded || token_real(c.a0, c.a1, c.a2, r, g);
+  const float inv = real ? 1.f / l : 0.f;
   for (int d = 0; d < D; ++d) o[base + row * D + d] = acc[d] * inv;
-  if (lse) lse[((size_t)b * Hh + hh) * g.S + row] = m + logf(l);
+  if (lse) lse[((size_t)b * Hh + hh) * g.S + row] = real ? m + logf(l) : 0.f;
 }
 
 // Dl_i = <dO_i, O_i>, one thread per row.
@@ -143,7 +147,8 @@ __global__ __launch_bounds__(kRows) void dq_f32_kernel(
   for (int i0 = 0; i0 < w0; ++i0)
     for (int i1 = 0; i1 < w1; ++i1)
       for (int i2 = 0; i2 < w2; ++i2) {
-        const int kt = ((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2);
+        const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
+        const int kt = (k0 * g.n1 + k1) * g.n2 + k2;
         for (int j0 = 0; j0 < g.L; j0 += kChunk) {
           const int nk = min(kChunk, g.L - j0);
           __syncthreads();
@@ -154,6 +159,7 @@ __global__ __launch_bounds__(kRows) void dq_f32_kernel(
           }
           __syncthreads();
           for (int j = 0; j < nk; ++j) {
+            if (g.padded && !token_real(k0, k1, k2, j0 + j, g)) continue;  // padding key
             float s = 0.f, dp = 0.f;
             for (int d = 0; d < D; ++d) {
               s = fmaf(qv[d], ks[j][d], s);
@@ -166,7 +172,8 @@ __global__ __launch_bounds__(kRows) void dq_f32_kernel(
         }
       }
   if (!active) return;
-  for (int d = 0; d < D; ++d) dq[base + row * D + d] = acc[d];
+  const bool real = !g.padded || token_real(c.a0, c.a1, c.a2, r, g);
+  for (int d = 0; d < D; ++d) dq[base + row * D + d] = real ? acc[d] : 0.f;
 }
 
 // dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i over the query tiles
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(kRows) void dkv_f32_kernel(
           }
           __syncthreads();
           for (int i = 0; i < nq; ++i) {
+            if (g.padded && !token_real(q0, q1, q2, i0 + i, g)) continue;  // padding query
             float s = 0.f, dp = 0.f;
             for (int d = 0; d < D; ++d) {
               s = fmaf(qs[i][d], kv[d], s);
@@ -239,9 +247,10 @@ __global__ __launch_bounds__(kRows) void dkv_f32_kernel(
         }
       }
   if (!active) return;
+  const bool real = !g.padded || token_real(c.a0, c.a1, c.a2, r, g);
   for (int d = 0; d < D; ++d) {
-    dk[base + row * D + d] = ak[d];
-    dv[base + row * D + d] = av[d];
+    dk[base + row * D + d] = real ? ak[d] : 0.f;
+    dv[base + row * D + d] = real ? av[d] : 0.f;
   }
 }
 

@@ -206,6 +206,32 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
   auto issue = [&](char* kl, char* vl) { copier.issue(kb, vb, (size_t)next_key0(), kl, vl); };
 
+  // Padded latents: keys at padding positions of a partial key tile are masked
+  // out of the stage being computed (a second walk over the key blocks).
+  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  auto mask_keys = [&](f32x16 (&sacc)[QT]) {
+    if (!g.padded) return;
+    const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
+    if (tile_partial(k0, k1, k2, g)) {
+      const uint32_t bits = block_real_bits(k0, k1, k2, cjb * KB, g, lane);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
+    }
+    if (++cjb == bpt) {
+      cjb = 0;
+      if (++ci2 == w2) {
+        ci2 = 0;
+        if (++ci1 == w1) {
+          ci1 = 0;
+          ++ci0;
+        }
+      }
+    }
+  };
+
   f32x16 oacc[QT][C::DT];
   float mrun[QT], lrun[QT];
 #pragma unroll
@@ -240,6 +266,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
                    const char* vl_nxt, char* kl_far, char* vl_far) {
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
+    mask_keys(sacc);
     bf16x8 pf[QT][2];
     // Raised wave priority during the vector work: when the two waves of a
     // SIMD compete for issue, the one in its softmax goes first and the
@@ -268,11 +295,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     stage(j + 3, vfb, vfa, kl0, vl0, kl2, vl2);
   }
 
-  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; zero on padding rows.
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float lt = xsum32(lrun[qt]);
-    const float inv = 1.0f / lt;
+    const int rin = qrow0 - qtile * g.L + qt * 32 + c32;  // row inside the query tile
+    const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
+    const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow0 + qt * 32 + c32;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -283,7 +312,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qt][dt][4 * i + j] * inv);
         *(bf16x4*)(o + row * D + dt * 32 + 8 * i + 4 * grp) = w;
       }
-    if (lse != nullptr && grp == 0) lse[row] = (mrun[qt] + log2f(lt)) * kLn2;
+    if (lse != nullptr && grp == 0) lse[row] = real ? (mrun[qt] + log2f(lt)) * kLn2 : 0.0f;
   }
 }
 

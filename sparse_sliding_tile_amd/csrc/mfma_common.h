@@ -100,6 +100,22 @@ constexpr int dma_kv_per_wave() {
   return (2 * (ROWS / (1024 / (D * 2)))) / NW;
 }
 
+// Padding mask of one 32-row block of an MFMA accumulator, whose element
+// 4i + j in lane l holds row 8i + 4(l / 32) + j.  The rows are the intra-tile
+// positions row0 .. row0 + 31 of tile (a0, a1, a2); bit 8i + j of the result
+// is set when the token of element 4i + j is real.  Every lane must call it
+// (it is a ballot).
+__device__ __forceinline__ uint32_t block_real_bits(int a0, int a1, int a2, int row0,
+                                                    const Geometry& g, int lane) {
+  const bool real = token_real(a0, a1, a2, row0 + (lane & 31), g);
+  const uint32_t m = (uint32_t)__ballot(real);
+  return m >> (4 * (lane >> 5));
+}
+
+__device__ __forceinline__ bool elem_real(uint32_t bits, int e) {
+  return (bits >> (8 * (e >> 2) + (e & 3))) & 1u;
+}
+
 // x combined with the value of lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float xmax32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

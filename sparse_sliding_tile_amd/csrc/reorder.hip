@@ -5,7 +5,10 @@
 // tile is made one contiguous run of the sequence).  A bit-exact gather/scatter
 // bound by HBM bandwidth: one workgroup moves one tile of one (batch, head); the
 // w tokens of a tile row are contiguous in both orders, so every wavefront reads
-// and writes whole token rows with 16-byte accesses.
+// and writes whole token rows with 16-byte accesses.  A latent that is not a
+// whole number of tiles is padded with masking (OpenReview rebuttal, answer on
+// input resolution): the reorder writes zero rows at padding positions of the
+// tile-major tensor and the unreorder skips them.
 #include "kernels.h"
 
 namespace sta {
@@ -37,14 +40,18 @@ __global__ __launch_bounds__(256) void tile_copy_kernel(const char* __restrict__
   const uint32_t a1 = a01 % g.n1;
   const uint32_t a0 = a01 / g.n1;
   const uint32_t units = (uint32_t)g.L * fd_units.d;
-  const uint64_t base = bh * (uint64_t)g.S * row_bytes;
+  const uint64_t rbase = bh * (uint64_t)g.Sr * row_bytes;  // raster tensor
+  const uint64_t tbase = bh * (uint64_t)g.S * row_bytes;   // tile-major tensor
+  const int e0 = tile_ext(a0, g.t, g.T), e1 = tile_ext(a1, g.h, g.H), e2 = tile_ext(a2, g.w, g.W);
 
   for (uint32_t u0 = threadIdx.x; u0 < units; u0 += 256 * U) {
     V val[U];
     uint64_t doff[U];
+    bool store[U];
 #pragma unroll
     for (int e = 0; e < U; ++e) {
       const uint32_t u = u0 + e * 256;
+      store[e] = false;
       if (u < units) {
         const uint32_t i = fdiv(u, fd_units);          // token inside the tile
         const uint32_t c = u - i * fd_units.d;         // chunk inside the token row
@@ -52,17 +59,21 @@ __global__ __launch_bounds__(256) void tile_copy_kernel(const char* __restrict__
         const uint32_t i2 = i - i01 * g.w;
         const uint32_t i0 = fdiv(i01, fd_h);
         const uint32_t i1 = i01 - i0 * g.h;
+        const bool real = (int)i0 < e0 && (int)i1 < e1 && (int)i2 < e2;
         const uint64_t raster =
             ((uint64_t)(a0 * g.t + i0) * g.H + (a1 * g.h + i1)) * g.W + (a2 * g.w + i2);
         const uint64_t tm = (uint64_t)tile * g.L + i;
-        const uint64_t soff = base + (to_tile_major ? raster : tm) * row_bytes + (uint64_t)c * G;
-        doff[e] = base + (to_tile_major ? tm : raster) * row_bytes + (uint64_t)c * G;
-        val[e] = __builtin_nontemporal_load((const V*)(src + soff));
+        const uint64_t roff = rbase + raster * row_bytes + (uint64_t)c * G;
+        const uint64_t toff = tbase + tm * row_bytes + (uint64_t)c * G;
+        doff[e] = to_tile_major ? toff : roff;
+        store[e] = real || to_tile_major;  // padding: zero in tile-major, nothing in raster
+        val[e] = V{};
+        if (real) val[e] = __builtin_nontemporal_load((const V*)(src + (to_tile_major ? roff : toff)));
       }
     }
 #pragma unroll
     for (int e = 0; e < U; ++e) {
-      if (u0 + e * 256 < units) __builtin_nontemporal_store(val[e], (V*)(dst + doff[e]));
+      if (store[e]) __builtin_nontemporal_store(val[e], (V*)(dst + doff[e]));
     }
   }
 }

@@ -36,6 +36,9 @@ WORKLOADS = {
                               head_dim=128, dtype="bf16", windows=[(3, 3, 5)] * 40),
     "finetune_24x64x64_w355": dict(latent=(24, 64, 64), tile=(6, 8, 8), batch=1, heads=24,
                                    head_dim=128, dtype="bf16", windows=[(3, 5, 5)] * 24),
+    # Padding with masking, the pages' example: (29, 45, 76) padded to (30, 48, 80).
+    "hunyuan_29x45x76_w333_padded": dict(latent=(29, 45, 76), tile=(6, 8, 8), batch=1, heads=24,
+                                         head_dim=128, dtype="bf16", windows=[(3, 3, 3)] * 24),
     # 2D STA (T = 1, an image latent): 128 x 128 tokens, tile (1, 8, 8) = 64
     # tokens, window 5 x 5 tiles.
     "image_2d_1x128x128_w155": dict(latent=(1, 128, 128), tile=(1, 8, 8), batch=1, heads=24,

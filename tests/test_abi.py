@@ -10,6 +10,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 import oracle as O
@@ -72,9 +73,9 @@ def test_forward_argument_errors(lib):
     assert fwd(lib, scale=-1.0) == ARG
     assert fwd(lib, scale=float("nan")) == ARG
     assert fwd(lib, B=0) == ARG
-    assert fwd(lib, latent=(5, 16, 16)) == NOT_MULT          # [STA-rebut]: whole tiles only
-    assert fwd(lib, latent=(29, 45, 76), tile=(6, 8, 8)) == NOT_MULT
     assert fwd(lib, latent=(0, 16, 16)) == ARG
+    assert fwd(lib, latent=(5, 16, 16), windows=((3, 0, 3), (3, 3, 3))) == WINDOW   # padded latent, bad window
+    assert fwd(lib, latent=(2000, 2000, 2000), tile=(6, 8, 8)) == TOO_LARGE
     assert fwd(lib, windows=((3, 0, 3), (3, 3, 3))) == WINDOW
     assert fwd(lib, windows=((3, 3, 3), (3, 3, -1))) == WINDOW
     assert fwd(lib, D=96) == UNSUP                             # bf16 needs D in {64, 128}
@@ -91,7 +92,7 @@ def test_forward_argument_errors(lib):
 def test_reorder_argument_errors(lib):
     f = lib.sta_tile_reorder
     assert f(NUL, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ARG
-    assert f(P, P, 1, 2, 64, d3(6, 16, 15), d3(2, 4, 4), 0, NUL) == NOT_MULT
+    assert f(P, P, 1, 2, 64, d3(1, 2, 1 << 30), d3(1, 1, 3), 0, NUL) == TOO_LARGE
     assert f(MIS, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ALIGN
     assert f(P, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 9, NUL) == UNSUP
     assert lib.sta_tile_unreorder(P, NUL, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ARG
@@ -101,9 +102,12 @@ def test_reorder_argument_errors(lib):
 def test_backward_argument_errors(lib):
     w = win([(3, 3, 3)] * 2)
     wp = w.ctypes.data_as(ctypes.c_void_p)
-    need = lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), 0)
-    assert need == 2 * 1 * 2 * 1536 * 4 + 2 * (1536 // 32) * 4   # row statistics + key-tile order
-    assert lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), 1) == 2 * 1 * 2 * 1536 * 4
+    need = lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), d3(2, 4, 4), 0)
+    assert need == 2 * 1 * 2 * 1536 * 4 + 2 * 48 * 4   # row statistics + key-tile order (48 tiles)
+    assert lib.sta_backward_workspace_bytes(1, 2, 128, d3(6, 16, 16), d3(2, 4, 4), 1) == 2 * 1 * 2 * 1536 * 4
+    # padded latent (5, 15, 16) -> (6, 16, 16): sizes follow the padded sequence
+    assert lib.sta_backward_workspace_bytes(1, 2, 128, d3(5, 15, 16), d3(2, 4, 4), 0) == need
+    assert lib.sta_backward_workspace_bytes(1, 2, 128, d3(0, 15, 16), d3(2, 4, 4), 0) == 0
 
     def bwd(ws=P, nbytes=need, lse=P, dq=P, D=128, dt=0, windows=wp):
         return lib.sta_backward(P, P, P, P, P, lse, dq, P, P, ws, nbytes, 1, 2, D, d3(6, 16, 16), d3(2, 4, 4),
@@ -128,7 +132,7 @@ def test_dense_argument_errors(lib):
 def test_pairs_argument_errors(lib):
     w = win([(3, 3, 3)])
     wp = w.ctypes.data_as(ctypes.c_void_p)
-    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(4, 4, 4), wp, 1) == NOT_MULT
+    assert lib.sta_tile_pairs_count(d3(0, 16, 16), d3(4, 4, 4), wp, 1) == ARG
     assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), NUL, 1) == ARG
     bad = win([(0, 3, 3)])
     assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), bad.ctypes.data_as(ctypes.c_void_p), 1) == WINDOW
@@ -141,12 +145,14 @@ PAIR_CASES = [((6, 16, 16), (2, 4, 4), [(3, 3, 3), (1, 2, 5)]),
               ((24, 48, 80), (6, 8, 8), [(3, 3, 5)]),
               ((24, 64, 64), (6, 8, 8), [(3, 5, 5)]),
               ((5, 6, 10), (5, 3, 2), [(2, 2, 4), (9, 1, 1)]),
-              ((1, 8, 16), (1, 8, 8), [(1, 1, 1), (1, 1, 2)])]
+              ((1, 8, 16), (1, 8, 8), [(1, 1, 1), (1, 1, 2)]),
+              ((29, 45, 76), (6, 8, 8), [(3, 3, 3), (1, 6, 10)]),     # padded to (30, 48, 80)
+              ((5, 15, 13), (2, 4, 4), [(3, 3, 3), (2, 1, 4)])]       # padded to (6, 16, 16)
 
 
 @pytest.mark.parametrize("latent,tile,wins", PAIR_CASES)
 def test_pair_count_matches_oracle(latent, tile, wins):
-    _, off = O.tile_pairs(latent, tile, wins)
+    _, off = O.tile_pairs(O.padded_latent(latent, tile), tile, wins)
     assert L.tile_pairs_count(latent, tile, wins) == off[-1]
 
 
@@ -154,7 +160,7 @@ def test_pair_count_matches_oracle(latent, tile, wins):
 @pytest.mark.parametrize("transpose", [False, True])
 def test_host_pairs_bit_exact(latent, tile, wins, transpose):
     p, off = L.tile_pairs_host(latent, tile, wins, transpose=transpose)
-    rp, roff = O.tile_pairs(latent, tile, wins, transpose=transpose)
+    rp, roff = O.tile_pairs(O.padded_latent(latent, tile), tile, wins, transpose=transpose)
     assert np.array_equal(off, roff)
     assert np.array_equal(p, rp)
 
@@ -174,3 +180,14 @@ def test_product_never_imports_oracle():
                 text = open(os.path.join(dirpath, f), errors="replace").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_binding_validates_shapes():
+    """The binding checks tensor rows against the latent before any call (the
+    C entry points take sizes, not tensors)."""
+    x = torch.zeros((1, 1, 10, 8))
+    with pytest.raises((ValueError, TypeError)):
+        L.tile_reorder(x, (2, 2, 3), (1, 2, 2))        # 12 tokens expected
+    assert L.raster_len((29, 45, 76)) == 29 * 45 * 76
+    assert L.tile_major_len((29, 45, 76), (6, 8, 8)) == 30 * 48 * 80
+    assert L.tile_major_len((30, 48, 80), (6, 8, 8)) == 30 * 48 * 80

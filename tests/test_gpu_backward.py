@@ -31,6 +31,8 @@ BWD_SMALL = [  # latent, tile, B, windows, D
     ((12, 16, 24), (6, 8, 8), 1, [(1, 3, 3), (2, 2, 2)], 128),     # L = 384
     ((6, 32, 32), (2, 8, 8), 1, [(3, 1, 3)], 64),
     ((1, 32, 40), (1, 8, 8), 2, [(1, 3, 3), (1, 2, 4)], 128),     # 2D, L = 64
+    ((5, 15, 13), (2, 4, 4), 1, [(3, 3, 3), (2, 1, 4)], 128),     # padded to (6, 16, 16)
+    ((11, 30, 29), (2, 8, 8), 1, [(3, 3, 3)], 128),               # padded, L = 128
 ]
 
 
@@ -42,7 +44,8 @@ def test_backward_bf16_small(sta, latent, tile, B, wins, D):
     q, k, v, do = (_tm(sta, x[n], latent, tile) for n in ("q", "k", "v", "do"))
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
     dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
-    ref = O.backward(to64(q), to64(k), to64(v), to64(do), latent, tile, wins, scale)
+    ref = O.backward(*(O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v", "do")),
+                     latent, tile, wins, scale)
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         e = err_report(to64(got), r)
         print(name, e)
@@ -59,7 +62,8 @@ def test_backward_bf16_zero_query(sta):
     k, v, do = (_tm(sta, x[n], latent, tile) for n in ("k", "v", "do"))
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=0.088)
     _, _, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=0.088)
-    _, _, rdv = O.backward(np.zeros((1, 2, S, 128)), to64(k), to64(v), to64(do), latent, tile, wins, 0.088)
+    rk, rv, rdo = (O.reorder(to64(x[n]), latent, tile) for n in ("k", "v", "do"))
+    _, _, rdv = O.backward(np.zeros((1, 2, S, 128)), rk, rv, rdo, latent, tile, wins, 0.088)
     e = err_report(to64(dv), rdv)
     print(e)
     assert e["max_abs"] < 4e-3 and e["rel_rms"] < BF16_REL_RMS
@@ -77,7 +81,6 @@ def test_backward_bf16_finetune_sampled(sta):
     scale = D ** -0.5
     x = I.workload_inputs(name, with_do=True)
     q, k, v, do = (_tm(sta, x[nm], latent, tile) for nm in ("q", "k", "v", "do"))
-    del x
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
     dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
     torch.cuda.synchronize()
@@ -93,7 +96,8 @@ def test_backward_bf16_finetune_sampled(sta):
     qrows = np.r_[0:16, L - 16:L + 16, (n[0] * n[1] * n[2] - 1) * L:(n[0] * n[1] * n[2] - 1) * L + 16]
     krows = np.r_[0:16, L - 16:L]           # tile 0: seen by 2*3*3 query tiles
     for h in heads:
-        hq, hk, hv, hdo = (to64(t[:, h:h + 1]) for t in (q, k, v, do))
+        hq, hk, hv, hdo = (O.pad_reorder(to64(x[nm][:, h:h + 1]), latent, tile)
+                           for nm in ("q", "k", "v", "do"))
         rdq = O.backward_query_rows(hq, hk, hv, hdo, latent, tile, wins[h], scale, 0, 0, qrows)
         e = err_report(to64(dq[0, h, torch.from_numpy(qrows).cuda()]), rdq)
         print("head", h, "dq", e)
@@ -121,7 +125,6 @@ def test_backward_bf16_hunyuan_mixed_sampled(sta):
     scale = D ** -0.5
     x = I.workload_inputs(name, seed=2, with_do=True)
     q, k, v, do = (_tm(sta, x[nm], latent, tile) for nm in ("q", "k", "v", "do"))
-    del x
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
     dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
     torch.cuda.synchronize()
@@ -134,7 +137,8 @@ def test_backward_bf16_hunyuan_mixed_sampled(sta):
     qrows = np.r_[0:8, 150 * L - 8:150 * L + 8, (n[0] * n[1] * n[2] - 1) * L:(n[0] * n[1] * n[2] - 1) * L + 8]
     krows = np.r_[0:8, L - 8:L]           # key tile 0
     for h in heads:
-        hq, hk, hv, hdo = (to64(t[:, h:h + 1]) for t in (q, k, v, do))
+        hq, hk, hv, hdo = (O.pad_reorder(to64(x[nm][:, h:h + 1]), latent, tile)
+                           for nm in ("q", "k", "v", "do"))
         rdq = O.backward_query_rows(hq, hk, hv, hdo, latent, tile, wins[h], scale, 0, 0, qrows)
         e = err_report(to64(dq[0, h, torch.from_numpy(qrows).cuda()]), rdq)
         print("head", h, wins[h], "dq", e)

@@ -31,7 +31,10 @@ REORDER_CASES = [((6, 16, 16), (2, 4, 4), 1, 2, 64, torch.float32),
                  ((6, 16, 16), (2, 4, 4), 2, 3, 128, torch.bfloat16),
                  ((5, 6, 10), (5, 3, 2), 1, 2, 24, torch.bfloat16),     # ragged rows: 48-byte tokens
                  ((3, 4, 5), (1, 1, 1), 2, 1, 7, torch.float32),       # 28-byte rows, identity order
-                 ((30, 48, 80), (6, 8, 8), 1, 2, 128, torch.bfloat16)]
+                 ((30, 48, 80), (6, 8, 8), 1, 2, 128, torch.bfloat16),
+                 ((5, 15, 13), (2, 4, 4), 2, 2, 64, torch.bfloat16),    # padded to (6, 16, 16)
+                 ((5, 6, 9), (5, 3, 2), 1, 2, 24, torch.float32),      # padded, ragged rows
+                 ((29, 45, 76), (6, 8, 8), 1, 1, 128, torch.bfloat16)]  # the pages' padding example
 
 
 @pytest.mark.parametrize("latent,tile,B,Hh,D,dtype", REORDER_CASES)
@@ -40,7 +43,7 @@ def test_reorder_bit_exact(sta, latent, tile, B, Hh, D, dtype):
     g = torch.Generator().manual_seed(3)
     x = torch.randn((B, Hh, S, D), generator=g).to(dtype)
     y = sta.tile_reorder(_dev(x), latent, tile)
-    ref = O.reorder(bits(x), latent, tile)
+    ref = O.pad_reorder(bits(x), latent, tile)     # padding rows zero
     assert np.array_equal(bits(y), ref)
     back = sta.tile_unreorder(y, latent, tile)
     assert np.array_equal(bits(back), bits(x))
@@ -92,7 +95,7 @@ def test_forward_f32_tiny(sta):
     latent, tile, wins = w["latent"], w["tile"], w["windows"]
     q, k, v = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v"))
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=64 ** -0.5)
-    rq, rk, rv = (O.reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
+    rq, rk, rv = (O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
     ro, rl = O.forward(rq, rk, rv, latent, tile, wins, 64 ** -0.5)
     assert err_report(to64(o), ro)["max_abs"] < F32_TOL
     assert err_report(to64(lse), rl)["max_abs"] < F32_TOL
@@ -111,7 +114,7 @@ def test_backward_f32_tiny(sta):
     q, k, v, do = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v", "do"))
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
     dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
-    rq, rk, rv, rdo = (O.reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v", "do"))
+    rq, rk, rv, rdo = (O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v", "do"))
     ref = O.backward(rq, rk, rv, rdo, latent, tile, wins, scale)
     for got, r in zip((dq, dk, dv), ref):
         assert err_report(to64(got), r)["max_abs"] < F32_TOL
@@ -127,6 +130,9 @@ BF16_SMALL = [  # latent, tile, B, windows, D   (tile volume 32 and 128; several
     ((6, 32, 32), (2, 8, 8), 1, [(3, 3, 3), (1, 4, 2)], 64),
     ((1, 32, 40), (1, 8, 8), 2, [(1, 3, 3), (1, 1, 5), (1, 9, 9)], 128),   # 2D, L = 64
     ((1, 24, 40), (1, 8, 8), 1, [(1, 3, 3), (2, 2, 2)], 64),               # 2D, L = 64, D = 64
+    ((5, 15, 13), (2, 4, 4), 2, [(3, 3, 3), (2, 1, 4)], 128),              # padded to (6, 16, 16)
+    ((11, 30, 29), (2, 8, 8), 1, [(3, 3, 3), (1, 2, 4)], 128),             # padded, L = 128
+    ((5, 16, 20), (1, 8, 8), 1, [(3, 3, 3)], 64),                          # padded, L = 64
 ]
 
 
@@ -137,7 +143,7 @@ def test_forward_bf16_small(sta, latent, tile, B, wins, D):
     scale = D ** -0.5
     q, k, v = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v"))
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
-    rq, rk, rv = (O.reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
+    rq, rk, rv = (O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
     ro, rl = O.forward(rq, rk, rv, latent, tile, wins, scale)
     eo, el = err_report(to64(o), ro), err_report(to64(lse), rl)
     print("O", eo, "LSE", el)
@@ -154,7 +160,8 @@ def test_forward_bf16_zero_query_window_mean(sta):
     q = torch.zeros((1, 2, S, 128), dtype=torch.bfloat16, device="cuda")
     k, v = (_tile_major(sta, x[n], latent, tile) for n in ("k", "v"))
     o, lse = sta.forward(q, k, v, latent, tile, wins, scale=0.088)
-    ro, rl = O.forward(np.zeros((1, 2, S, 128)), to64(k), to64(v), latent, tile, wins, 0.088)
+    rk, rv = (O.reorder(to64(x[n]), latent, tile) for n in ("k", "v"))
+    ro, rl = O.forward(np.zeros((1, 2, S, 128)), rk, rv, latent, tile, wins, 0.088)
     e = err_report(to64(o), ro)
     print(e)
     assert e["max_abs"] < 4e-3
@@ -164,7 +171,7 @@ def test_forward_bf16_zero_query_window_mean(sta):
 def _check_sampled(sta, name, heads, rows_per_tile=32, seed=0):
     w = I.WORKLOADS[name]
     latent, tile, wins, D = w["latent"], w["tile"], w["windows"], w["head_dim"]
-    n, L = O.tile_grid(latent, tile)
+    n, L = O.tile_grid(O.padded_latent(latent, tile), tile)
     x = I.workload_inputs(name)
     scale = D ** -0.5
     q, k, v = (_tile_major(sta, x[nm], latent, tile) for nm in ("q", "k", "v"))
@@ -176,7 +183,7 @@ def _check_sampled(sta, name, heads, rows_per_tile=32, seed=0):
     rt = torch.from_numpy(rows).cuda()
     worst = {}
     for h in heads:
-        hq, hk, hv = (to64(t[:, h:h + 1]) for t in (q, k, v))
+        hq, hk, hv = (O.pad_reorder(to64(x[nm][:, h:h + 1]), latent, tile) for nm in ("q", "k", "v"))
         ro, rl = O.forward(hq, hk, hv, latent, tile, [wins[h]], scale, rows=rows)
         eo = err_report(to64(o[:, h:h + 1, rt]), ro)
         el = err_report(to64(lse[:, h:h + 1, rt]), rl)
@@ -205,13 +212,36 @@ def test_forward_bf16_image_2d_sampled(sta):
     _check_sampled(sta, "image_2d_1x128x128_w155", heads=[0, 23])
 
 
+def test_forward_bf16_padded_29x45x76_sampled(sta):
+    """The pages' padding example: a (29,45,76) latent padded to (30,48,80).
+    The sampled tiles include the last tile, whose tail rows are padding."""
+    _check_sampled(sta, "hunyuan_29x45x76_w333_padded", heads=[0, 23])
+
+
+def test_forward_backward_f32_padded(sta):
+    """fp32 debug instance on a padded latent at 1e-5, forward and backward."""
+    latent, tile, wins, scale = (5, 15, 13), (2, 4, 4), [(3, 3, 3), (2, 1, 4)], 0.2
+    x = I.make_inputs(1, 2, 5 * 15 * 13, 32, "f32", seed=11, with_do=True)
+    q, k, v, do = (_tile_major(sta, x[n], latent, tile) for n in ("q", "k", "v", "do"))
+    o, lse = sta.forward(q, k, v, latent, tile, wins, scale=scale)
+    dq, dk, dv = sta.backward(q, k, v, o, do, lse, latent, tile, wins, scale=scale)
+    rq, rk, rv, rdo = (O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v", "do"))
+    ro, rl = O.forward(rq, rk, rv, latent, tile, wins, scale)
+    assert err_report(to64(o), ro)["max_abs"] < F32_TOL
+    assert err_report(to64(lse), rl)["max_abs"] < F32_TOL
+    for got, r in zip((dq, dk, dv), O.backward(rq, rk, rv, rdo, latent, tile, wins, scale)):
+        assert err_report(to64(got), r)["max_abs"] < F32_TOL
+    back = sta.tile_unreorder(o, latent, tile)
+    assert np.array_equal(bits(back), O.pad_unreorder(bits(o), latent, tile))
+
+
 # ------------------------------------------------------------------ dense
 
 def test_dense_bf16_small(sta):
     x = I.make_inputs(1, 2, 1536, 128, "bf16", seed=7)
     q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
     o, lse = sta.dense_forward(q, k, v, scale=128 ** -0.5)
-    ro, rl = O.dense_forward(to64(q), to64(k), to64(v), 128 ** -0.5)
+    ro, rl = O.dense_forward(to64(x["q"]), to64(x["k"]), to64(x["v"]), 128 ** -0.5)
     eo = err_report(to64(o), ro)
     assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
     assert err_report(to64(lse), rl)["max_abs"] < BF16_TOL
@@ -221,6 +251,6 @@ def test_dense_f32_small(sta):
     x = I.make_inputs(1, 2, 640, 64, "f32", seed=8)
     q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
     o, lse = sta.dense_forward(q, k, v, scale=0.125)
-    ro, rl = O.dense_forward(to64(q), to64(k), to64(v), 0.125)
+    ro, rl = O.dense_forward(to64(x["q"]), to64(x["k"]), to64(x["v"]), 0.125)
     assert err_report(to64(o), ro)["max_abs"] < F32_TOL
     assert err_report(to64(lse), rl)["max_abs"] < F32_TOL
