@@ -14,9 +14,9 @@
 //   3. dV and 4. dK: key-tile-major, walking the query tiles whose window
 //             holds the key tile (an interval per dimension): S = Q K^T,
 //             dP = dO V^T (lane = key), dV += P^T dO, dK += dS^T Q.  That count
-//             varies several-fold between edge and centre tiles, so workgroups
-//             are launched heaviest first (rank-major over all heads) and dealt
-//             round-robin to the XCDs, which keeps the tail of the launch short.
+//             varies several-fold between edge and centre tiles, so within
+//             each head workgroups are launched heaviest first, heads one after
+//             the other (cache locality), dealt round-robin to the XCDs.
 // Every (query tile, key tile) pair is a full dense block, as in the forward.
 // The operand layouts, LDS swizzle and transposed reads are those of
 // mfma_common.h; a transposed read of a row-major [32 x D] tile gives the
@@ -98,9 +98,12 @@ __global__ __launch_bounds__(256) void bwd_rank_kernel(Geometry g, HeadTable ht,
   }
 }
 
-// Key-major work item: items are (rank, head slot, batch, sub-block), rank
-// slowest, so the heaviest key tiles of every head go first; consecutive
-// workgroups land on different XCDs (blockIdx round-robin).
+// Key-major work item: items are (head slot, rank, batch, sub-block), head
+// slowest: the workgroups running at one time belong to one or two heads and
+// share those heads' Q and dO in the caches, and within a head the heaviest
+// key tiles go first, so each head's light tiles fill the gaps while the next
+// head starts.  Consecutive workgroups land on different XCDs (blockIdx
+// round-robin).
 struct KeyItem {
   int b, head, ktile, sub;
 };
@@ -111,10 +114,10 @@ __device__ __forceinline__ KeyItem key_major_item(const int32_t* __restrict__ ra
   KeyItem it;
   it.sub = item % blocks_per_tile;
   item /= blocks_per_tile;
-  const uint32_t hb = item % (uint32_t)(B * Hh);
-  const int rank = item / (uint32_t)(B * Hh);
-  it.b = hb % B;
-  it.head = ht.order[hb / B];
+  it.b = item % B;
+  item /= B;
+  const int rank = item % g.ntiles;
+  it.head = ht.order[item / g.ntiles];
   it.ktile = rank_tab[(size_t)it.head * g.ntiles + rank];
   return it;
 }
