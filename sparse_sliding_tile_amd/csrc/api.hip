@@ -44,6 +44,8 @@ int make_geometry(sta_dim3 latent, sta_dim3 tile, Geometry* g) {
   g->Sr = latent.t * latent.h * latent.w;
   g->ntiles = g->n0 * g->n1 * g->n2;
   g->padded = (latent.t % tile.t || latent.h % tile.h || latent.w % tile.w) ? 1 : 0;
+  g->fw = make_fastdiv((uint32_t)tile.w);
+  g->fhw = make_fastdiv((uint32_t)(tile.h * tile.w));
   return STA_OK;
 }
 

@@ -39,49 +39,6 @@ STA_HD void window_transpose(int k, int wp, int n, int* lo, int* hi) {
   *hi = b;
 }
 
-// Per-launch geometry, passed by value in the kernel arguments.
-struct Geometry {
-  int T, H, W;     // latent (real tokens)
-  int t, h, w;     // tile
-  int n0, n1, n2;  // tile grid, ceil(latent / tile) per dimension
-  int L;           // tokens per tile
-  int S;           // tile-major rows per (b, head): n0 * n1 * n2 * L
-  int Sr;          // raster rows per (b, head): T * H * W
-  int ntiles;      // n0 * n1 * n2
-  int padded;      // 1 when the latent is not a whole number of tiles
-};
-
-// Padding with masking ("Fast Video Generation with Sliding Tile Attention",
-// OpenReview rebuttal, answer on input resolution): a latent that is not a
-// whole number of tiles is padded up to the next multiple in each dimension.
-// Tile a then holds real tokens only in the box of intra-tile coordinates
-// [0, ext) per dimension, ext = min(tile, latent - a * tile); the other
-// positions are padding: never keys, and their output rows are zero.
-STA_HD int tile_ext(int a, int tile, int latent) {
-  const int e = latent - a * tile;
-  return e < tile ? e : tile;
-}
-
-STA_HD bool tile_partial(int a0, int a1, int a2, const Geometry& g) {
-  return tile_ext(a0, g.t, g.T) < g.t || tile_ext(a1, g.h, g.H) < g.h ||
-         tile_ext(a2, g.w, g.W) < g.w;
-}
-
-// Whether intra-tile position i (raster order inside the tile) of tile
-// (a0, a1, a2) holds a real token.
-STA_HD bool token_real(int a0, int a1, int a2, int i, const Geometry& g) {
-  const int i2 = i % g.w, i1 = (i / g.w) % g.h, i0 = i / (g.w * g.h);
-  return i0 < tile_ext(a0, g.t, g.T) && i1 < tile_ext(a1, g.h, g.H) && i2 < tile_ext(a2, g.w, g.W);
-}
-
-// Per-head windows, already clamped to the grid (w'), plus a launch order of
-// the heads (heaviest first) for load balance.  Lives in the kernel arguments,
-// so each launch carries its own copy.
-struct HeadTable {
-  uint16_t wp[STA_MAX_HEADS][3];
-  uint8_t order[STA_MAX_HEADS];
-};
-
 // ---------------------------------------------------------------------------
 // Unsigned division by a run-time invariant d >= 1 for 0 <= n < 2^31, with a
 // multiply-high and a shift (Granlund & Montgomery, "Division by invariant
@@ -110,6 +67,51 @@ STA_HD uint32_t fdiv(uint32_t n, FastDiv f) {
 #endif
   return (hi + n) >> f.l;
 }
+
+// Per-launch geometry, passed by value in the kernel arguments.
+struct Geometry {
+  int T, H, W;     // latent (real tokens)
+  int t, h, w;     // tile
+  int n0, n1, n2;  // tile grid, ceil(latent / tile) per dimension
+  int L;           // tokens per tile
+  int S;           // tile-major rows per (b, head): n0 * n1 * n2 * L
+  int Sr;          // raster rows per (b, head): T * H * W
+  int ntiles;      // n0 * n1 * n2
+  int padded;      // 1 when the latent is not a whole number of tiles
+  FastDiv fw, fhw; // division by w and by h * w (intra-tile coordinates)
+};
+
+// Padding with masking ("Fast Video Generation with Sliding Tile Attention",
+// OpenReview rebuttal, answer on input resolution): a latent that is not a
+// whole number of tiles is padded up to the next multiple in each dimension.
+// Tile a then holds real tokens only in the box of intra-tile coordinates
+// [0, ext) per dimension, ext = min(tile, latent - a * tile); the other
+// positions are padding: never keys, and their output rows are zero.
+STA_HD int tile_ext(int a, int tile, int latent) {
+  const int e = latent - a * tile;
+  return e < tile ? e : tile;
+}
+
+STA_HD bool tile_partial(int a0, int a1, int a2, const Geometry& g) {
+  return tile_ext(a0, g.t, g.T) < g.t || tile_ext(a1, g.h, g.H) < g.h ||
+         tile_ext(a2, g.w, g.W) < g.w;
+}
+
+// Whether intra-tile position i (raster order inside the tile) of tile
+// (a0, a1, a2) holds a real token.
+STA_HD bool token_real(int a0, int a1, int a2, int i, const Geometry& g) {
+  const uint32_t i01 = fdiv((uint32_t)i, g.fw), i0 = fdiv((uint32_t)i, g.fhw);
+  const int i2 = i - (int)i01 * g.w, i1 = (int)i01 - (int)i0 * g.h;
+  return (int)i0 < tile_ext(a0, g.t, g.T) && i1 < tile_ext(a1, g.h, g.H) && i2 < tile_ext(a2, g.w, g.W);
+}
+
+// Per-head windows, already clamped to the grid (w'), plus a launch order of
+// the heads (heaviest first) for load balance.  Lives in the kernel arguments,
+// so each launch carries its own copy.
+struct HeadTable {
+  uint16_t wp[STA_MAX_HEADS][3];
+  uint8_t order[STA_MAX_HEADS];
+};
 
 // ---------------------------------------------------------------------------
 // Vector types for MFMA operands and 16-byte memory traffic.
