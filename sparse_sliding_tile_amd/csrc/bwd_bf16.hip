@@ -227,10 +227,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
     if (!g.padded) return;
     const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
     if (tile_partial(k0, k1, k2, g)) {
-      const uint32_t bits = block_real_bits(k0, k1, k2, cjb * kStage, g, lane);
+      const uint32_t m = block_real_mask(k0, k1, k2, cjb * kStage, g, lane);
+      if (m != 0xffffffffu) {
+        const uint32_t bits = lane_bits(m, lane);
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (!elem_real(bits, e)) st[e] = -INFINITY;
+        for (int e = 0; e < 16; ++e)
+          if (!elem_real(bits, e)) st[e] = -INFINITY;
+      }
     }
     if (++cjb == spt) {
       cjb = 0;
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     uint32_t bits = 0xffffffffu;
     if (!g.padded) return bits;
     const int q0 = lo0 + ci0, q1 = lo1 + ci1, q2 = lo2 + ci2;
-    if (tile_partial(q0, q1, q2, g)) bits = block_real_bits(q0, q1, q2, cjb * kStage, g, lane);
+    if (tile_partial(q0, q1, q2, g)) bits = lane_bits(block_real_mask(q0, q1, q2, cjb * kStage, g, lane), lane);
     if (++cjb == spt) {
       cjb = 0;
       if (++ci2 == c2) {
@@ -471,8 +474,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   // zero on padding rows.
   uint16_t* out = MODE == 0 ? dv : dk;
   const float osc = MODE == 0 ? 1.0f : scale;
-  const uint32_t kbits = g.padded ? block_real_bits(a0, a1, a2, sub * (NW * 32) + wave * 32, g, lane)
-                                  : 0xffffffffu;
+  const uint32_t kbits =
+      g.padded ? lane_bits(block_real_mask(a0, a1, a2, sub * (NW * 32) + wave * 32, g, lane), lane)
+               : 0xffffffffu;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll

@@ -213,12 +213,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     if (!g.padded) return;
     const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
     if (tile_partial(k0, k1, k2, g)) {
-      const uint32_t bits = block_real_bits(k0, k1, k2, cjb * KB, g, lane);
+      const uint32_t m = block_real_mask(k0, k1, k2, cjb * KB, g, lane);
+      if (m != 0xffffffffu) {  // blocks of a partial tile are often whole
+        const uint32_t bits = lane_bits(m, lane);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
+          for (int e = 0; e < 16; ++e)
+            if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
+      }
     }
     if (++cjb == bpt) {
       cjb = 0;

@@ -100,16 +100,20 @@ constexpr int dma_kv_per_wave() {
   return (2 * (ROWS / (1024 / (D * 2)))) / NW;
 }
 
-// Padding mask of one 32-row block of an MFMA accumulator, whose element
-// 4i + j in lane l holds row 8i + 4(l / 32) + j.  The rows are the intra-tile
-// positions row0 .. row0 + 31 of tile (a0, a1, a2); bit 8i + j of the result
-// is set when the token of element 4i + j is real.  Every lane must call it
-// (it is a ballot).
-__device__ __forceinline__ uint32_t block_real_bits(int a0, int a1, int a2, int row0,
+// Padding mask of one 32-row block: bit r is set when intra-tile position
+// row0 + r of tile (a0, a1, a2) holds a real token.  The same value in every
+// lane (a ballot; every lane must call it).
+__device__ __forceinline__ uint32_t block_real_mask(int a0, int a1, int a2, int row0,
                                                     const Geometry& g, int lane) {
   const bool real = token_real(a0, a1, a2, row0 + (lane & 31), g);
-  const uint32_t m = (uint32_t)__ballot(real);
-  return m >> (4 * (lane >> 5));
+  return (uint32_t)__ballot(real);
+}
+
+// The block mask seen from an MFMA accumulator whose element 4i + j in lane l
+// holds row 8i + 4(l / 32) + j: bit 8i + j of the result belongs to element
+// 4i + j (test it with elem_real).
+__device__ __forceinline__ uint32_t lane_bits(uint32_t block_mask, int lane) {
+  return block_mask >> (4 * (lane >> 5));
 }
 
 __device__ __forceinline__ bool elem_real(uint32_t bits, int e) {
