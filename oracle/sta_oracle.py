@@ -31,6 +31,11 @@ the pages are silent (each is listed in the design doc as well):
     on the low side);
   * windows are counted in tiles; a window < 1 is an error;
   * the log-sum-exp uses the natural logarithm;
+  * the per-head window search ([STA-meth]: each head gets its own window,
+    chosen automatically) is measured by the attention mass a candidate window
+    keeps: the share of a head's full (unmasked) softmax probability whose keys
+    lie in the window, averaged over the real queries.  How a window is then
+    picked from these numbers needs the model and is not part of the oracle;
   * a latent that is not a whole number of tiles is handled as [STA-rebut]'s
     "padding with masking": it is padded up to the next tile multiple in each
     dimension, windows live on the padded tile grid, padding tokens are never
@@ -47,6 +52,7 @@ __all__ = [
     "pad_reorder", "pad_unreorder", "window_start",
     "window_contains", "tile_pairs", "token_tile_coords", "window_mask",
     "forward", "backward", "backward_key_rows", "backward_query_rows", "dense_forward",
+    "window_mass",
 ]
 
 
@@ -425,3 +431,44 @@ def dense_forward(q, k, v, scale, rows=None, chunk=256):
                 o[b, h, c0:c0 + r.size] = (e @ v[b, h]) / l
                 lse[b, h, c0:c0 + r.size] = (mx + np.log(l))[:, 0]
     return o, lse
+
+
+def window_mass(q, k, latent, tile, candidates, scale, order="tile", chunk=256):
+    """Attention mass of candidate windows, per head, float64.
+
+    [STA-abs]: attention in pretrained video models concentrates in local 3D
+    windows; [STA-meth]: the window is configured per head.  The quantity that
+    compares candidate windows of one head is the share of its full attention
+    that a window keeps.  For query row i of (batch b, head h):
+      P_ij = exp(s_ij) / sum_j' exp(s_ij'),  s_ij = scale * <q_i, k_j>,
+    over every real key j (no window), and
+      mass_i(w) = sum of P_ij over the keys j whose tile lies in window w of
+                  the tile of i.
+    Returns mass[c, b, h] = mean of mass_i(candidates[c]) over the real query
+    rows of (b, h).  On a padded latent, padding positions are neither keys nor
+    queries.
+    """
+    grid, valid = _padding(latent, tile, order)
+    B, Hh, S, D = q.shape
+    if k.shape != q.shape:
+        raise ValueError("q and k must share one [B, Hh, S, D] shape")
+    cands = np.asarray(candidates).reshape(-1, 3)
+    if cands.shape[0] < 1:
+        raise ValueError("at least one candidate window")
+    q, k = (np.asarray(a, dtype=np.float64) for a in (q, k))
+    real = np.ones(S, dtype=bool) if valid is None else valid
+    rows_all = np.flatnonzero(real)
+    total = np.zeros((cands.shape[0], B, Hh))
+    for c0 in range(0, rows_all.size, chunk):
+        r = rows_all[c0:c0 + chunk]
+        masks = [window_mask(grid, tile, cands[c], order, rows=r) & real[None, :]
+                 for c in range(cands.shape[0])]
+        for b in range(B):
+            for h in range(Hh):
+                s = scale * (q[b, h, r] @ k[b, h].T)
+                s[:, ~real] = -np.inf
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                for c, m in enumerate(masks):
+                    total[c, b, h] += p[m].sum()
+    return total / rows_all.size

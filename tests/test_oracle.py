@@ -570,3 +570,100 @@ def test_padded_backward_matches_autograd():
     dk_rows, dv_rows = O.backward_key_rows(*args, latent, tile, wins[1], scale, 1, 1, rows)
     np.testing.assert_allclose(dk_rows, got[1][1, 1], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv_rows, got[2][1, 1], rtol=0, atol=1e-12)
+
+
+# --- attention mass of candidate windows (per-head window search) ---------
+
+def _brute_force_mass(q, k, latent, tile, cands, scale):
+    """Mass by scalar loops: full softmax of each real query over every real
+    key with math.exp, then the probabilities of keys in the window summed.
+    Raster order; padded latents slide windows on the ceil grid."""
+    T, H, W = latent
+    t, h, w = tile
+    n = (-(-T // t), -(-H // h), -(-W // w))
+    B, Hh, S, D = q.shape
+    tc = [(tau // t, y // h, x // w) for tau in range(T) for y in range(H) for x in range(W)]
+    out = np.zeros((len(cands), B, Hh))
+    for c, win in enumerate(cands):
+        wins_d = [[_window_by_sliding(qq, win[d], n[d]) for qq in range(n[d])] for d in range(3)]
+        for b in range(B):
+            for hh in range(Hh):
+                tot = 0.0
+                for i in range(S):
+                    s = [scale * sum(q[b, hh, i, x] * k[b, hh, j, x] for x in range(D)) for j in range(S)]
+                    mx = max(s)
+                    e = [math.exp(x - mx) for x in s]
+                    inside = sum(e[j] for j in range(S)
+                                 if all(tc[j][d] in wins_d[d][tc[i][d]] for d in range(3)))
+                    tot += inside / sum(e)
+                out[c, b, hh] = tot / S
+    return out
+
+
+def test_window_mass_matches_brute_force():
+    latent, tile = (4, 8, 8), (2, 4, 4)     # tile grid 2x2x2, 256 tokens
+    cands = [(1, 1, 1), (2, 1, 2), (1, 2, 1), (9, 9, 9)]
+    q, k = (_rand((2, 2, 256, 3), s) for s in (71, 72))
+    ref = _brute_force_mass(q, k, latent, tile, cands, 0.8)
+    got = O.window_mass(q, k, latent, tile, cands, 0.8, order="raster")
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    qt, kt = (O.reorder(a, latent, tile) for a in (q, k))
+    np.testing.assert_allclose(O.window_mass(qt, kt, latent, tile, cands, 0.8), ref, rtol=0, atol=1e-12)
+
+
+def test_window_mass_padded_matches_brute_force():
+    cands = [(1, 1, 1), (1, 2, 1), (2, 3, 2)]
+    q, k = (_rand((1, 2, 90, 4), s) for s in (73, 74))
+    ref = _brute_force_mass(q, k, PAD_LATENT, PAD_TILE, cands, 0.6)
+    qt, kt = (O.pad_reorder(a, PAD_LATENT, PAD_TILE) for a in (q, k))
+    got = O.window_mass(qt, kt, PAD_LATENT, PAD_TILE, cands, 0.6)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_window_mass_full_window_is_one():
+    latent, tile = (6, 8, 12), (2, 4, 4)    # grid 3x2x3
+    q, k = (_rand((1, 3, 576, 8), s) for s in (75, 76))
+    got = O.window_mass(q, k, latent, tile, [(3, 2, 3), (7, 7, 7)], 0.4)
+    np.testing.assert_allclose(got, 1.0, rtol=0, atol=1e-12)
+
+
+def test_window_mass_uniform_attention_counts_keys():
+    # Q = 0: attention is uniform over the real keys, so a window keeps the
+    # fraction of real keys lying in it.
+    latent, tile = (6, 8, 12), (2, 4, 4)    # grid 3x2x3, L = 32
+    k = _rand((1, 1, 576, 4), 77)
+    got = O.window_mass(np.zeros_like(k), k, latent, tile, [(1, 1, 1), (3, 1, 2), (2, 2, 2)], 1.0)
+    np.testing.assert_allclose(got[:, 0, 0], [1 / 18, 6 / 18, 8 / 18], rtol=0, atol=1e-12)
+    # padded: count real keys per window tile by tile
+    kp = O.pad_reorder(_rand((1, 1, 90, 4), 78), PAD_LATENT, PAD_TILE)
+    cands = [(1, 1, 1), (1, 2, 1)]
+    got = O.window_mass(np.zeros_like(kp), kp, PAD_LATENT, PAD_TILE, cands, 1.0)
+    grid = O.padded_latent(PAD_LATENT, PAD_TILE)
+    n, L = O.tile_grid(grid, PAD_TILE)
+    real = O.valid_positions(PAD_LATENT, PAD_TILE).reshape(-1, L)
+    tiles = list(itertools.product(*(range(x) for x in n)))
+    for c, win in enumerate(cands):
+        num = 0.0
+        for qi, qt in enumerate(tiles):
+            keys = sum(real[ki].sum() for ki, kt in enumerate(tiles) if O.window_contains(qt, kt, win, n))
+            num += real[qi].sum() * keys / real.sum()
+        assert got[c, 0, 0] == pytest.approx(num / real.sum(), abs=1e-12)
+
+
+def test_window_mass_is_exp_of_lse_difference():
+    # The window's softmax normaliser against the full one: mass_i = exp(LSE_w - LSE_full).
+    latent, tile = (6, 8, 12), (2, 4, 4)
+    q, k, v = (_rand((2, 2, 576, 8), s) for s in (79, 80, 81))
+    win = (2, 1, 2)
+    _, lw = O.forward(q, k, v, latent, tile, [win] * 2, 0.5)
+    _, lf = O.dense_forward(q, k, v, 0.5)
+    ref = np.exp(lw - lf).mean(axis=2)
+    np.testing.assert_allclose(O.window_mass(q, k, latent, tile, [win], 0.5)[0], ref, rtol=0, atol=1e-12)
+
+
+def test_window_mass_grows_with_nested_windows():
+    latent, tile = (10, 8, 12), (2, 4, 4)   # grid 5x2x3
+    q, k = (_rand((1, 2, 960, 4), s) for s in (82, 83))
+    m = O.window_mass(q, k, latent, tile, [(1, 1, 1), (3, 1, 1), (3, 1, 3), (5, 2, 3)], 1.0)
+    assert np.all(np.diff(m[:, 0, :], axis=0) > 0)
+    np.testing.assert_allclose(m[-1], 1.0, rtol=0, atol=1e-12)
