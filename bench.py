@@ -294,6 +294,31 @@ def main():
                 "pct_of_peak": round(100 * bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "counted": "10*L^2*D per tile pair (5 GEMMs); the kernels run 8 (dQ, dV and dK passes)"}
             del a, b_, c, do, out, ll, ws
+        # window search, measurement side: attention mass of the five
+        # candidate windows of the mixed-window workload, all 24 heads
+        sw = I.WORKLOADS["hunyuan_30x48x80_w333"]
+        sS = sta.tile_major_len(sw["latent"], sw["tile"])
+        shape = (sw["batch"], sw["heads"], sS, sw["head_dim"])
+        a, b_ = rand(shape), rand(shape)
+        cands = [(5, 6, 10), (3, 3, 3), (3, 3, 5), (5, 3, 3), (1, 6, 10)]
+        ws = torch.empty(sta.window_mass_workspace_bytes(shape[0], shape[1], sw["latent"], sw["tile"]),
+                         dtype=torch.uint8, device=dev)
+        mass = sta.window_mass(a, b_, sw["latent"], sw["tile"], cands, workspace=ws)
+        t = Timer(torch)
+        for _ in range(2):
+            with t:
+                sta.window_mass(a, b_, sw["latent"], sw["tile"], cands, workspace=ws, out=mass)
+        torch.cuda.synchronize()
+        sms = t.total_ms() / 2
+        # counted: Q K^T only (2*L^2*D per tile pair) for the full-window pass and each candidate
+        sflops = sum(fwd_flops(sw["latent"], sw["tile"], [c] * shape[1], shape[0], shape[3]) // 2
+                     for c in [(5, 6, 10)] + cands)
+        legs["window_mass_5_candidates"] = {
+            "ms": round(sms, 3), "tflops": round(sflops / sms / 1e9, 1),
+            "pct_of_peak": round(100 * sflops / sms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "mean_mass": [round(float(x_), 4) for x_ in mass.mean(dim=(1, 2)).tolist()],
+            "counted": "2*L^2*D per tile pair (Q K^T) for the full window and each candidate"}
+        del a, b_, ws, mass
         result["legs"] = legs
 
     print(json.dumps(result), flush=True)

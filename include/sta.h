@@ -150,6 +150,34 @@ int sta_backward(const void* q, const void* k, const void* v, const void* o, con
 int sta_dense_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                       int64_t Hh, int64_t S, int64_t D, float scale, sta_dtype dt, void* stream);
 
+/* Bytes of device workspace sta_window_mass needs: 8*B*Hh*S' (two fp32
+ * log-sum-exp vectors over the tile-major rows).  0 for invalid sizes. */
+size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, sta_dim3 tile);
+
+/* Attention mass of candidate windows, the measurement side of the per-head
+ * window search ([STA-meth]: each head gets its own window, configured
+ * automatically; [STA-abs]: attention concentrates in local 3D windows).
+ * For query row i of (batch b, head h), with s_ij = scale <q_i, k_j> over ALL
+ * real keys j, the share of the full softmax that candidate window w keeps is
+ *   mass_i(w) = sum_{j in w} exp(s_ij) / sum_j exp(s_ij)
+ *             = exp(LSE_w,i - LSE_full,i),
+ * and mass[c][b][h] (fp32, device, n_cand*B*Hh values, fully overwritten) is
+ * its mean over the real query rows of (b, h) for window cand_host[c].
+ * q, k: tile-major [B, Hh, S', D] of type dt (as for sta_forward; V is not
+ * needed).  cand_host: host int32 [n_cand][3] windows in tiles, each >= 1,
+ * clamped to the grid, the same for every head; read during the call.
+ * workspace: device memory of at least sta_window_mass_workspace_bytes(),
+ * caller-owned, contents on entry irrelevant; on return it holds the per-row
+ * statistics: fp32 [B, Hh, S'] LSE of the full window, then fp32 [B, Hh, S']
+ * LSE of the last candidate (natural log, tile-major rows, 0 on padding
+ * rows).  The work is one normaliser-only
+ * forward pass with the full window plus one per candidate, each followed by a
+ * per-(b, h) mean.  Errors as sta_forward, plus STA_ERR_WORKSPACE. */
+int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, size_t ws_bytes,
+                    int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                    const int32_t* cand_host, int64_t n_cand, float scale, sta_dtype dt,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

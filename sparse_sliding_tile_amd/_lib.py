@@ -39,6 +39,9 @@ SIGNATURES = {
                                     c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
     "sta_dense_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
                                          c_f32, ctypes.c_int, c_vp]),
+    "sta_window_mass_workspace_bytes": (c_sz, [c_i64, c_i64, Dim3, Dim3]),
+    "sta_window_mass": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_sz, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
+                                       c_i64, c_f32, ctypes.c_int, c_vp]),
 }
 
 _lib = None
@@ -252,3 +255,31 @@ def dense_forward(q, k, v, scale=None, out=None, want_lse=True):
     _check(lib().sta_dense_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, S, D,
                                    scale, _dtype(q), _stream(q)), "sta_dense_forward")
     return out, lse
+
+
+def window_mass_workspace_bytes(B, Hh, latent, tile):
+    return int(lib().sta_window_mass_workspace_bytes(B, Hh, _dim3(latent), _dim3(tile)))
+
+
+def window_mass(q, k, latent, tile, candidates, scale=None, workspace=None, out=None):
+    """Attention mass of each candidate window (one window for all heads at a
+    time) on tile-major q, k: float32 [C, B, Hh] on the device, the mean over
+    real query rows of the share of the full softmax the window keeps."""
+    B, Hh, S, D = _shape4(q, "q")
+    if S != tile_major_len(latent, tile):
+        raise ValueError(f"q has {S} rows, tile-major {latent}/{tile} has {tile_major_len(latent, tile)}")
+    _same(q.shape, "q", ("q", q), ("k", k))
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    c = np.ascontiguousarray(np.asarray(candidates, dtype=np.int32).reshape(-1, 3))
+    nbytes = window_mass_workspace_bytes(B, Hh, latent, tile)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    shape = (c.shape[0], B, Hh)
+    out = torch.empty(shape, dtype=torch.float32, device=q.device) if out is None else out
+    if tuple(out.shape) != shape or out.dtype != torch.float32:
+        raise ValueError(f"out must be float32 {shape}")
+    _check(lib().sta_window_mass(_dev(q, "q"), _dev(k, "k"), _dev(out, "mass"), _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), B, Hh, D, _dim3(latent),
+                                 _dim3(tile), c.ctypes.data_as(c_vp), c.shape[0], scale, _dtype(q), _stream(q)),
+           "sta_window_mass")
+    return out

@@ -283,4 +283,67 @@ int sta_dense_forward(const void* q, const void* k, const void* v, void* o, floa
   return forward_impl(q, k, v, o, lse, B, Hh, D, g, ht, scale, dt, stream);
 }
 
+size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, sta_dim3 tile) {
+  Geometry g;
+  if (B < 1 || Hh < 1 || make_geometry(latent, tile, &g) != STA_OK) return 0;
+  // Two fp32 log-sum-exp vectors over the tile-major rows: the full one and
+  // the candidate's.
+  return 2 * (size_t)B * Hh * (size_t)g.S * sizeof(float);
+}
+
+int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, size_t ws_bytes,
+                    int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                    const int32_t* cand_host, int64_t n_cand, float scale, sta_dtype dt,
+                    void* stream) {
+  Geometry g;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if (!q || !k || !mass || !cand_host || n_cand < 1) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
+  if ((st = check_sizes(B, Hh, D, g))) return st;
+  if (Hh > STA_MAX_HEADS) return STA_ERR_UNSUPPORTED;
+  if (n_cand * B * Hh >= (1ll << 31)) return STA_ERR_TOO_LARGE;
+  if (dt == STA_BF16) {
+    if (!fwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
+  } else if (dt == STA_F32) {
+    if (D != 32 && D != 64 && D != 128) return STA_ERR_UNSUPPORTED;
+  } else {
+    return STA_ERR_UNSUPPORTED;
+  }
+  if (!workspace || ws_bytes < sta_window_mass_workspace_bytes(B, Hh, latent, tile))
+    return STA_ERR_WORKSPACE;
+  if (misaligned(q) || misaligned(k) || misaligned(workspace)) return STA_ERR_ALIGN;
+  // Every table is built (and every window checked) before the first launch.
+  std::vector<int32_t> win(3 * (size_t)Hh);
+  for (int64_t h = 0; h < Hh; ++h) {
+    win[3 * h] = g.n0;
+    win[3 * h + 1] = g.n1;
+    win[3 * h + 2] = g.n2;
+  }
+  HeadTable full;
+  if ((st = make_heads(win.data(), Hh, g, &full))) return st;
+  std::vector<HeadTable> cands((size_t)n_cand);
+  for (int64_t c = 0; c < n_cand; ++c) {
+    for (int64_t h = 0; h < Hh; ++h)
+      for (int d = 0; d < 3; ++d) win[3 * h + d] = cand_host[3 * c + d];
+    if ((st = make_heads(win.data(), Hh, g, &cands[c]))) return st;
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  float* lse_full = (float*)workspace;
+  float* lse_win = lse_full + (size_t)B * Hh * g.S;
+  auto lse_pass = [&](const HeadTable& ht, float* out) {
+    if (dt == STA_BF16)
+      return launch_lse_bf16((const uint16_t*)q, (const uint16_t*)k, out, g, ht, (int)B, (int)Hh,
+                             (int)D, scale, s);
+    return launch_fwd_f32((const float*)q, (const float*)k, (const float*)k, nullptr, out, g, ht,
+                          (int)B, (int)Hh, (int)D, scale, s);
+  };
+  hipError_t e = lse_pass(full, lse_full);
+  for (int64_t c = 0; c < n_cand && e == hipSuccess; ++c) {
+    e = lse_pass(cands[c], lse_win);
+    if (e == hipSuccess) e = launch_mass(lse_win, lse_full, mass + c * B * Hh, g, B * Hh, s);
+  }
+  return to_status(e);
+}
+
 }  // extern "C"

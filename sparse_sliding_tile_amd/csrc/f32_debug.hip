@@ -22,7 +22,8 @@ __device__ __forceinline__ TileCoord tile_coord(int a, const Geometry& g) {
 }
 
 // Forward: O_i = sum_j softmax(scale q_i.k_j) v_j over the window's keys.
-template <int D>
+// LSE_ONLY computes the softmax normaliser alone (v and o are not touched).
+template <int D, bool LSE_ONLY>
 __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict__ q,
                                                         const float* __restrict__ k,
                                                         const float* __restrict__ v,
@@ -44,11 +45,10 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   const bool active = r < g.L;
   const size_t row = (size_t)qt * g.L + (active ? r : 0);
 
-  float qv[D], acc[D];
-  for (int d = 0; d < D; ++d) {
-    qv[d] = q[base + row * D + d];
-    acc[d] = 0.f;
-  }
+  float qv[D], acc[LSE_ONLY ? 1 : D];
+  for (int d = 0; d < D; ++d) qv[d] = q[base + row * D + d];
+  if constexpr (!LSE_ONLY)
+    for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m = -INFINITY, l = 0.f;
 
   const TileCoord c = tile_coord(qt, g);
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
           for (int x = threadIdx.x; x < nk * D; x += kRows) {
             const size_t kr = (size_t)kt * g.L + j0 + x / D;
             ks[x / D][x % D] = k[base + kr * D + x % D];
-            vs[x / D][x % D] = v[base + kr * D + x % D];
+            if constexpr (!LSE_ONLY) vs[x / D][x % D] = v[base + kr * D + x % D];
           }
           __syncthreads();
           float s[kChunk];
@@ -81,11 +81,13 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
           const float mn = fmaxf(m, mc);
           const float corr = expf(m - mn);
           l *= corr;
-          for (int d = 0; d < D; ++d) acc[d] *= corr;
+          if constexpr (!LSE_ONLY)
+            for (int d = 0; d < D; ++d) acc[d] *= corr;
           for (int j = 0; j < nk; ++j) {
             const float p = expf(s[j] - mn);  // 0 for a masked key
             l += p;
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[j][d], acc[d]);
+            if constexpr (!LSE_ONLY)
+              for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[j][d], acc[d]);
           }
           m = mn;
         }
@@ -93,8 +95,10 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   if (!active) return;
   // Padding rows (padded latents) are no query: zero output.
   const bool real = !g.padded || token_real(c.a0, c.a1, c.a2, r, g);
-  const float inv = real ? 1.f / l : 0.f;
-  for (int d = 0; d < D; ++d) o[base + row * D + d] = acc[d] * inv;
+  if constexpr (!LSE_ONLY) {
+    const float inv = real ? 1.f / l : 0.f;
+    for (int d = 0; d < D; ++d) o[base + row * D + d] = acc[d] * inv;
+  }
   if (lse) lse[((size_t)b * Hh + hh) * g.S + row] = real ? m + logf(l) : 0.f;
 }
 
@@ -259,8 +263,13 @@ hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, f
                      const Geometry& g, const HeadTable& ht, int B, int Hh, float scale,
                      hipStream_t st) {
   const int subs = (g.L + kRows - 1) / kRows;
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((uint32_t)(B * Hh * g.ntiles * subs)), dim3(kRows),
-                     0, st, q, k, v, o, lse, g, ht, Hh, scale);
+  const dim3 grid((uint32_t)(B * Hh * g.ntiles * subs));
+  if (o == nullptr)
+    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), grid, dim3(kRows), 0, st, q, k, v, o, lse, g, ht,
+                       Hh, scale);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), grid, dim3(kRows), 0, st, q, k, v, o, lse, g,
+                       ht, Hh, scale);
   return hipGetLastError();
 }
 

@@ -107,6 +107,29 @@ __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (
   }
 }
 
+// Softmax normaliser only (no P V): running maximum and fp32 row sum of the
+// exponentials, with the same lazy rescale.
+template <int QT>
+__device__ __forceinline__ void lse_stage(const f32x16 (&sacc)[QT], float (&mrun)[QT],
+                                          float (&lrun)[QT], float c_log2) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx = sacc[qt][0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[qt][e]);
+    const float mblk = xmax32(mx) * c_log2;
+    if (mblk > mrun[qt] + kRescaleThreshold) {
+      lrun[qt] *= __builtin_amdgcn_exp2f(mrun[qt] - mblk);
+      mrun[qt] = mblk;
+    }
+    const float mneg = -mrun[qt];
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ls += __builtin_amdgcn_exp2f(fmaf(sacc[qt][e], c_log2, mneg));
+    lrun[qt] += ls;
+  }
+}
+
 // O^T += V^T P^T for one stage.
 template <int D, int QT>
 __device__ __forceinline__ void pv_stage(const bf16x8 (&vf)[D / 32][2], const bf16x8 (&pf)[QT][2],
@@ -119,7 +142,8 @@ __device__ __forceinline__ void pv_stage(const bf16x8 (&vf)[D / 32][2], const bf
       for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma32(vf[dt][s], pf[qt][s], oacc[qt][dt]);
 }
 
-template <int D, int QT, int NW, int OCC>
+// LSE_ONLY: the log-sum-exp alone (v and o unused): K blocks only, no P V.
+template <int D, int QT, int NW, int OCC, bool LSE_ONLY>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, Geometry g,
@@ -204,7 +228,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     return key0;
   };
   const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
-  auto issue = [&](char* kl, char* vl) { copier.issue(kb, vb, (size_t)next_key0(), kl, vl); };
+  auto issue = [&](char* kl, char* vl) {
+    if constexpr (LSE_ONLY) copier.issue_k(kb, (size_t)next_key0(), kl);
+    else copier.issue(kb, vb, (size_t)next_key0(), kl, vl);
+  };
 
   // Padded latents: keys at padding positions of a partial key tile are masked
   // out of the stage being computed (a second walk over the key blocks).
@@ -251,7 +278,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // j + 1 (leaving the copy of j + 2 in flight), barrier (all waves are past
   // stage j - 1, so buffer (j + 3) % 4 is free), start the copy of j + 3, read
   // the K fragments of j + 1 (they land during P V), and P V of j.
-  constexpr int PER = KvDma<D, KB, NW>::PER;
+  constexpr int PER = LSE_ONLY ? KvDma<D, KB, NW>::PT : KvDma<D, KB, NW>::PER;
   issue(kl0, vl0);
   if (nblk > 1) issue(kl1, vl1);
   if (nblk > 2) issue(kl2, vl2);
@@ -263,13 +290,25 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // only then starts the next copy.
   bf16x8 kf[C::KS], vfa[C::DT][2], vfb[C::DT][2];
   read_rows<D>(kl0, kf, grp, c32);
-  read_cols<D>(vl0, vfa, lane);
+  if constexpr (!LSE_ONLY) read_cols<D>(vl0, vfa, lane);
 
   auto stage = [&](int j, bf16x8 (&vf)[C::DT][2], bf16x8 (&vf_nxt)[C::DT][2], const char* kl_nxt,
                    const char* vl_nxt, char* kl_far, char* vl_far) {
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
     mask_keys(sacc);
+    if constexpr (LSE_ONLY) {
+      lse_stage<QT>(sacc, mrun, lrun, c_log2);
+      if (j + 1 < nblk) {
+        if (j + 2 < nblk) wait_dma_upto<PER>();
+        else wait_dma();
+        barrier_lds();
+        read_rows<D>(kl_nxt, kf, grp, c32);
+        asm volatile("" ::: "memory");
+        if (j + 3 < nblk) issue(kl_far, vl_far);
+      }
+      return;
+    }
     bf16x8 pf[QT][2];
     // Raised wave priority during the vector work: when the two waves of a
     // SIMD compete for issue, the one in its softmax goes first and the
@@ -306,15 +345,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
     const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow0 + qt * 32 + c32;
+    if constexpr (!LSE_ONLY) {
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 w;
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qt][dt][4 * i + j] * inv);
-        *(bf16x4*)(o + row * D + dt * 32 + 8 * i + 4 * grp) = w;
-      }
+          for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qt][dt][4 * i + j] * inv);
+          *(bf16x4*)(o + row * D + dt * 32 + 8 * i + 4 * grp) = w;
+        }
+    }
     if (lse != nullptr && grp == 0) lse[row] = real ? (mrun[qt] + log2f(lt)) * kLn2 : 0.0f;
   }
 }
@@ -328,7 +369,7 @@ inline int xcd_group_items(int seqs, int items_per_seq) {
   return 0;
 }
 
-template <int D, int QT, int NW, int OCC>
+template <int D, int QT, int NW, int OCC, bool LSE_ONLY = false>
 hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                       float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                       float scale, hipStream_t st) {
@@ -336,7 +377,7 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
   const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC>), dim3((uint32_t)total),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, LSE_ONLY>), dim3((uint32_t)total),
                      dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, B, Hh, scale * kLog2e, bpt,
                      total, group);
   return hipGetLastError();
@@ -359,6 +400,26 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
     if (L % 128 == 0) return launch_cfg<64, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
     if (L % 64 == 0) return launch_cfg<64, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
     return launch_cfg<64, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, const Geometry& g,
+                           const HeadTable& ht, int B, int Hh, int D, float scale, hipStream_t st) {
+  const int L = g.L;
+  if (D == 128) {
+    if (L % 128 == 0)
+      return launch_cfg<128, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+    if (L % 64 == 0)
+      return launch_cfg<128, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<128, 1, 1, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+  }
+  if (D == 64) {
+    if (L % 128 == 0)
+      return launch_cfg<64, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+    if (L % 64 == 0)
+      return launch_cfg<64, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<64, 1, 1, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
   }
   return hipErrorInvalidValue;
 }

@@ -13,7 +13,8 @@ hipError_t launch_tile_pairs(int32_t* out, const Geometry& g, const HeadTable& h
                              int transpose, hipStream_t stream);
 void host_tile_pairs(int32_t* out, const Geometry& g, const HeadTable& ht, int Hh, int transpose);
 
-// fp32 debug instance (D in {32, 64, 128}).
+// fp32 debug instance (D in {32, 64, 128}).  o == nullptr computes the LSE
+// alone (v is then not read).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
                           float scale, hipStream_t stream);
@@ -27,11 +28,18 @@ bool fwd_bf16_supported(int D, int L);
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                            int D, float scale, hipStream_t stream);
+// The forward's log-sum-exp alone (no P V, V not read).
+hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, const Geometry& g,
+                           const HeadTable& ht, int B, int Hh, int D, float scale, hipStream_t stream);
 bool bwd_bf16_supported(int D, int L);
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const uint16_t* dout, const float* lse,
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dl,
                            const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
                            float scale, hipStream_t stream);
+
+// mass[bh] = mean over the real rows of sequence bh of exp(lse_win - lse_full).
+hipError_t launch_mass(const float* lse_win, const float* lse_full, float* mass, const Geometry& g,
+                       int64_t BH, hipStream_t stream);
 
 }  // namespace sta

@@ -193,6 +193,12 @@ struct KvDma {
       dma16(vbase + goff[e], vl + seg * 1024);
     }
   }
+  // The K block alone (PT copies per wave).
+  __device__ __forceinline__ void issue_k(const uint16_t* kg, size_t row0, char* kl) const {
+    const char* kbase = (const char*)(kg + row0 * D);
+#pragma unroll
+    for (int e = 0; e < PT; ++e) dma16(kbase + goff[e], kl + (wave_u + e * NW) * 1024);
+  }
 };
 
 // A/B operand fragments of a row-major [32 x D] tile (rows = keys or

@@ -129,6 +129,32 @@ def test_dense_argument_errors(lib):
     assert f(P, P, P, P, NUL, 1, 2, 1024, 128, 0.0, 0, NUL) == ARG
 
 
+def test_window_mass_argument_errors(lib):
+    need = lib.sta_window_mass_workspace_bytes(1, 2, d3(6, 16, 16), d3(2, 4, 4))
+    assert need == 2 * 1 * 2 * 1536 * 4                      # two fp32 LSE vectors
+    assert lib.sta_window_mass_workspace_bytes(1, 2, d3(5, 15, 16), d3(2, 4, 4)) == need   # padded
+    assert lib.sta_window_mass_workspace_bytes(0, 2, d3(6, 16, 16), d3(2, 4, 4)) == 0
+    good = win([(3, 3, 3), (1, 1, 1)])
+    bad = win([(3, 3, 3), (1, 0, 1)])
+
+    def wm(q=P, k=P, mass=P, ws=P, nbytes=need, Hh=2, D=128, cands=good, n=2, scale=0.1, dt=0):
+        cp = cands.ctypes.data_as(ctypes.c_void_p) if cands is not None else NUL
+        return lib.sta_window_mass(q, k, mass, ws, nbytes, 1, Hh, D, d3(6, 16, 16), d3(2, 4, 4), cp, n,
+                                   scale, dt, NUL)
+    assert wm(q=NUL) == ARG
+    assert wm(mass=NUL) == ARG
+    assert wm(cands=None) == ARG
+    assert wm(n=0) == ARG
+    assert wm(scale=0.0) == ARG
+    assert wm(ws=NUL) == WS
+    assert wm(nbytes=need - 1) == WS
+    assert wm(D=96) == UNSUP
+    assert wm(dt=5) == UNSUP
+    assert wm(q=MIS) == ALIGN
+    assert wm(cands=bad) == WINDOW          # every candidate is checked before the first launch
+    assert wm(Hh=257) == UNSUP
+
+
 def test_pairs_argument_errors(lib):
     w = win([(3, 3, 3)])
     wp = w.ctypes.data_as(ctypes.c_void_p)
