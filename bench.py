@@ -319,6 +319,25 @@ def main():
             "mean_mass": [round(float(x_), 4) for x_ in mass.mean(dim=(1, 2)).tolist()],
             "counted": "2*L^2*D per tile pair (Q K^T) for the full window and each candidate"}
         del a, b_, ws, mass
+        # the matrix cores alone on N(0, 1) bf16 operands and on zeros: the rate
+        # the power limit leaves on data like the inputs, next to the nominal peak
+        ceil = {}
+        for kind in ("randn", "zeros"):
+            ops = rand((1 << 19,)) if kind == "randn" else torch.zeros(1 << 19, dtype=torch.bfloat16, device=dev)
+            cout, cfl = sta.calib_mfma_bf16(ops, 20000, 512)
+            for _ in range(60):
+                sta.calib_mfma_bf16(ops, 20000, 512, out=cout)
+            t = Timer(torch)
+            for _ in range(40):
+                with t:
+                    sta.calib_mfma_bf16(ops, 20000, 512, out=cout)
+            torch.cuda.synchronize()
+            ceil[kind] = cfl / (t.total_ms() / 40) / 1e9
+            del ops, cout
+        legs["mfma_calibration"] = {
+            "tflops_randn_operands": round(ceil["randn"], 1), "tflops_zero_operands": round(ceil["zeros"], 1),
+            "sta_forward_frac_of_randn_rate": round(achieved / ceil["randn"], 3),
+            "note": "bf16 32x32x16 MFMA loop, 2 waves per SIMD, no memory traffic"}
         result["legs"] = legs
 
     print(json.dumps(result), flush=True)

@@ -178,6 +178,20 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
                     const int32_t* cand_host, int64_t n_cand, float scale, sta_dtype dt,
                     void* stream);
 
+/* Measurement support, not part of the method: a bf16 matrix-core loop
+ * (v_mfma_f32_32x32x16_bf16, 16 per thread per iteration, four independent
+ * accumulator chains, no memory traffic) whose operands are taken from the
+ * caller's buffer, so its rate shows what the matrix cores sustain on data
+ * drawn like the attention inputs (their power draw, and with it the clock
+ * under the board's power limit, depends on the operand values).
+ * operands: device, operand_bytes a power of two >= 256 (16-byte aligned);
+ * blocks workgroups of 256 threads each run iters iterations: the launch does
+ * blocks*256/64 waves * iters * 16 * 32768 FLOP.  out: device fp32
+ * [blocks*256], overwritten with per-thread sums (so the work is kept).
+ * Asynchronous on stream; time it with events. */
+int sta_calib_mfma_bf16(const void* operands, int64_t operand_bytes, int64_t iters, int64_t blocks,
+                        float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

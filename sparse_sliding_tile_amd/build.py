@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsta.so")
-SOURCES = ["api.hip", "reorder.hip", "f32_debug.hip", "fwd_bf16.hip", "bwd_bf16.hip", "mass.hip"]
+SOURCES = ["api.hip", "reorder.hip", "f32_debug.hip", "fwd_bf16.hip", "bwd_bf16.hip", "mass.hip", "calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -346,4 +346,15 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
   return to_status(e);
 }
 
+int sta_calib_mfma_bf16(const void* operands, int64_t operand_bytes, int64_t iters, int64_t blocks,
+                        float* out, void* stream) {
+  if (!operands || !out || iters < 1 || blocks < 1) return STA_ERR_ARG;
+  const int64_t vecs = operand_bytes / 16;
+  if (vecs < 16 || (vecs & (vecs - 1)) != 0 || operand_bytes % 16 != 0) return STA_ERR_ARG;
+  if (iters >= (1ll << 31) || blocks >= (1ll << 31) / 256) return STA_ERR_TOO_LARGE;
+  if (misaligned(operands) || misaligned(out)) return STA_ERR_ALIGN;
+  return to_status(
+      launch_calib_mfma(operands, vecs, (int)iters, (int)blocks, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

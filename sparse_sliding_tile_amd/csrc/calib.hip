@@ -1,0 +1,52 @@
+// Matrix-core calibration loop: the bf16 MFMA rate this GPU sustains on
+// operands drawn like the attention inputs, with nothing else running.
+//
+// Not part of the attention method: it gives the measurement a second
+// reference next to the published dense peak.  Operand values decide how much
+// power the matrix cores draw, and under the board's power limit that sets the
+// clock; a loop on all-zero operands runs at the top clock, a loop on N(0, 1)
+// bf16 operands may not.  Each wave keeps eight A and eight B fragments (taken
+// from the caller's buffer) and cycles through them, so consecutive MFMAs see
+// different operands, in four independent accumulator chains.
+#include "kernels.h"
+#include "mfma_common.h"
+
+namespace sta {
+
+namespace {
+
+constexpr int kCalibThreads = 256;
+
+__global__ __launch_bounds__(kCalibThreads) void calib_mfma_kernel(const u32x4* __restrict__ src,
+                                                                   uint32_t src_mask, int iters,
+                                                                   float* __restrict__ out) {
+  const uint32_t t = blockIdx.x * kCalibThreads + threadIdx.x;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = as_bf16x8(src[(t * 16u + i) & src_mask]);
+    b[i] = as_bf16x8(src[(t * 16u + 8 + i) & src_mask]);
+  }
+  f32x16 acc[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i & 3] = mfma32(a[i], b[(i * 3) & 7], acc[i & 3]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i & 3] = mfma32(a[(i + 3) & 7], b[(i * 5) & 7], acc[i & 3]);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) r += acc[0][e] + acc[1][e] + acc[2][e] + acc[3][e];
+  out[t] = r;
+}
+
+}  // namespace
+
+hipError_t launch_calib_mfma(const void* src, int64_t src_vectors, int iters, int blocks, float* out,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(calib_mfma_kernel, dim3((uint32_t)blocks), dim3(kCalibThreads), 0, st,
+                     (const u32x4*)src, (uint32_t)(src_vectors - 1), iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace sta

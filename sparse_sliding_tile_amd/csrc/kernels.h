@@ -42,4 +42,9 @@ hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 hipError_t launch_mass(const float* lse_win, const float* lse_full, float* mass, const Geometry& g,
                        int64_t BH, hipStream_t stream);
 
+// Matrix-core calibration loop (blocks x 256 threads, 16 MFMAs per thread per
+// iteration); src holds src_vectors 16-byte operand vectors, a power of two.
+hipError_t launch_calib_mfma(const void* src, int64_t src_vectors, int iters, int blocks, float* out,
+                             hipStream_t stream);
+
 }  // namespace sta

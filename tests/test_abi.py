@@ -155,6 +155,17 @@ def test_window_mass_argument_errors(lib):
     assert wm(Hh=257) == UNSUP
 
 
+def test_calib_argument_errors(lib):
+    f = lib.sta_calib_mfma_bf16
+    assert f(NUL, 1 << 20, 10, 4, P, NUL) == ARG
+    assert f(P, 1 << 20, 10, 4, NUL, NUL) == ARG
+    assert f(P, 3 << 16, 10, 4, P, NUL) == ARG        # not a power of two
+    assert f(P, 128, 10, 4, P, NUL) == ARG            # fewer than 16 vectors
+    assert f(P, 1 << 20, 0, 4, P, NUL) == ARG
+    assert f(P, 1 << 20, 10, 1 << 40, P, NUL) == TOO_LARGE
+    assert f(MIS, 1 << 20, 10, 4, P, NUL) == ALIGN
+
+
 def test_pairs_argument_errors(lib):
     w = win([(3, 3, 3)])
     wp = w.ctypes.data_as(ctypes.c_void_p)
