@@ -272,22 +272,42 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     lrun[qt] = 0.f;
   }
 
-  // Pipeline over 32-key stages; stage j sits in LDS buffer j % 4 and its
-  // HBM->LDS copy is issued two stages ahead.  In stage j: read the V^T
-  // fragments of j, Q K^T and softmax of j, then wait for the copy of stage
-  // j + 1 (leaving the copy of j + 2 in flight), barrier (all waves are past
-  // stage j - 1, so buffer (j + 3) % 4 is free), start the copy of j + 3, read
-  // the K fragments of j + 1 (they land during P V), and P V of j.
+  // Pipeline over 32-key stages; stage j sits in LDS slot j % SLOTS.  Four
+  // slots for 4-wave workgroups; two for smaller workgroups, whose 64 KB
+  // four-slot ring would leave room for only two of them per CU (one wave per
+  // SIMD), while at 32 KB four fit and each SIMD runs two waves.  In stage j:
+  // Q K^T and softmax of j (its K fragments were read in stage j - 1); wait
+  // for the copy of stage j + 1 (with four slots the copy of j + 2 stays in
+  // flight); barrier; read the K and V^T fragments of j + 1; start the copy of
+  // stage j + AHEAD into the slot that is free: (j + 3) % 4, last read in
+  // stage j - 2, or with two slots j % 2, read in stage j - 1 (each wave waits
+  // for its own LDS reads before the barrier, so none is still in flight);
+  // then P V of j, overlapping the reads.
+  constexpr int SLOTS = NW >= 4 ? 4 : 2;
+  constexpr int AHEAD = SLOTS == 4 ? 3 : 2;
   constexpr int PER = LSE_ONLY ? KvDma<D, KB, NW>::PT : KvDma<D, KB, NW>::PER;
   issue(kl0, vl0);
   if (nblk > 1) issue(kl1, vl1);
-  if (nblk > 2) issue(kl2, vl2);
-  if (nblk > 2) wait_dma_upto<2 * PER>();
-  else wait_dma();
+  if constexpr (SLOTS == 4) {
+    if (nblk > 2) issue(kl2, vl2);
+    if (nblk > 2) wait_dma_upto<2 * PER>();
+    else wait_dma();
+  } else {
+    if (nblk > 1) wait_dma_upto<PER>();
+    else wait_dma();
+  }
   barrier_lds();
-  // A wave's LDS read issued after its own LDS copy waits for that copy to
-  // land, so each stage reads all its operands of the next stage first and
-  // only then starts the next copy.
+  auto wait_next = [&](int j) {
+    if constexpr (SLOTS == 4) {
+      if (j + 2 < nblk) wait_dma_upto<PER>();
+      else wait_dma();
+    } else {
+      wait_dma();
+      wait_lds();
+    }
+  };
+  // Each stage reads all its operands of the next stage before it starts a
+  // copy (reads behind the wave's own copy were measured slower).
   bf16x8 kf[C::KS], vfa[C::DT][2], vfb[C::DT][2];
   read_rows<D>(kl0, kf, grp, c32);
   if constexpr (!LSE_ONLY) read_cols<D>(vl0, vfa, lane);
@@ -300,12 +320,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     if constexpr (LSE_ONLY) {
       lse_stage<QT>(sacc, mrun, lrun, c_log2);
       if (j + 1 < nblk) {
-        if (j + 2 < nblk) wait_dma_upto<PER>();
-        else wait_dma();
+        wait_next(j);
         barrier_lds();
         read_rows<D>(kl_nxt, kf, grp, c32);
         asm volatile("" ::: "memory");
-        if (j + 3 < nblk) issue(kl_far, vl_far);
+        if (j + AHEAD < nblk) issue(kl_far, vl_far);
       }
       return;
     }
@@ -317,24 +336,34 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     softmax_stage<D, QT>(sacc, pf, oacc, mrun, lrun, c_log2);
     __builtin_amdgcn_s_setprio(0);
     if (j + 1 < nblk) {
-      if (j + 2 < nblk) wait_dma_upto<PER>();
-      else wait_dma();
+      wait_next(j);
       barrier_lds();
       read_rows<D>(kl_nxt, kf, grp, c32);
       read_cols<D>(vl_nxt, vf_nxt, lane);
       asm volatile("" ::: "memory");
-      if (j + 3 < nblk) issue(kl_far, vl_far);
+      if (j + AHEAD < nblk) issue(kl_far, vl_far);
     }
     pv_stage<D, QT>(vf, pf, oacc);
   };
-  for (int j = 0; j < nblk; j += 4) {
-    stage(j, vfa, vfb, kl1, vl1, kl3, vl3);
-    if (j + 1 >= nblk) break;
-    stage(j + 1, vfb, vfa, kl2, vl2, kl0, vl0);
-    if (j + 2 >= nblk) break;
-    stage(j + 2, vfa, vfb, kl3, vl3, kl1, vl1);
-    if (j + 3 >= nblk) break;
-    stage(j + 3, vfb, vfa, kl0, vl0, kl2, vl2);
+  if constexpr (SLOTS == 4) {
+    // stage j reads slot (j + 1) % 4 and refills slot (j + 3) % 4
+    for (int j = 0; j < nblk; j += 4) {
+      stage(j, vfa, vfb, kl1, vl1, kl3, vl3);
+      if (j + 1 >= nblk) break;
+      stage(j + 1, vfb, vfa, kl2, vl2, kl0, vl0);
+      if (j + 2 >= nblk) break;
+      stage(j + 2, vfa, vfb, kl3, vl3, kl1, vl1);
+      if (j + 3 >= nblk) break;
+      stage(j + 3, vfb, vfa, kl0, vl0, kl2, vl2);
+    }
+  } else {
+    // stage j reads slot (j + 1) % 2 and refills slot j % 2 (read by every
+    // wave one stage earlier)
+    for (int j = 0; j < nblk; j += 2) {
+      stage(j, vfa, vfb, kl1, vl1, kl0, vl0);
+      if (j + 1 >= nblk) break;
+      stage(j + 1, vfb, vfa, kl0, vl0, kl1, vl1);
+    }
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; zero on padding rows.
@@ -394,12 +423,12 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   if (D == 128) {
     if (L % 128 == 0) return launch_cfg<128, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
     if (L % 64 == 0) return launch_cfg<128, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<128, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<128, 1, 1, 1>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
   }
   if (D == 64) {
     if (L % 128 == 0) return launch_cfg<64, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
     if (L % 64 == 0) return launch_cfg<64, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<64, 1, 1, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<64, 1, 1, 1>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
   }
   return hipErrorInvalidValue;
 }
@@ -412,14 +441,14 @@ hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, con
       return launch_cfg<128, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
     if (L % 64 == 0)
       return launch_cfg<128, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<128, 1, 1, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<128, 1, 1, 1, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
   }
   if (D == 64) {
     if (L % 128 == 0)
       return launch_cfg<64, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
     if (L % 64 == 0)
       return launch_cfg<64, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<64, 1, 1, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<64, 1, 1, 1, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
   }
   return hipErrorInvalidValue;
 }
