@@ -161,16 +161,20 @@ def main():
     flops = fwd_flops(latent, tile, wins, B, D)
     fwd_timer = Timer(torch)
 
+    # One step is the whole forward path on raster-order tensors in one launch:
+    # the tile reorder of q, k, v and the unreorder of o happen in the kernel's
+    # own loads and stores (sta_forward_raster).  The same path with separate
+    # reorder kernels is timed as a leg.
     def step(timed):
-        sta.tile_reorder(q, latent, tile, out=qt)
-        sta.tile_reorder(k, latent, tile, out=kt)
-        sta.tile_reorder(v, latent, tile, out=vt)
         if timed:
             with fwd_timer:
-                sta.forward(qt, kt, vt, latent, tile, wins, out=ot, lse=lse)
+                sta.forward_raster(q, k, v, latent, tile, wins, out=o, lse=lse)
         else:
-            sta.forward(qt, kt, vt, latent, tile, wins, out=ot, lse=lse)
-        sta.tile_unreorder(ot, latent, tile, out=o)
+            sta.forward_raster(q, k, v, latent, tile, wins, out=o, lse=lse)
+
+    # A plain copy of known size (691,200 KiB read and written) in every run:
+    # the reference the FETCH_SIZE / WRITE_SIZE counters are scaled by.
+    sta.tile_reorder(q, latent, tile, out=qt)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -187,7 +191,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     fwd_ms = fwd_timer.total_ms() / args.steps
-    log(f"[bench] step {ms_step:.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms), sta_forward {fwd_ms:.3f} ms")
+    log(f"[bench] step {ms_step:.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms), forward kernel {fwd_ms:.3f} ms")
     achieved = flops / (fwd_ms * 1e-3) / 1e12
     traffic = read_traffic()
     result = {
@@ -205,11 +209,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "latent": list(latent), "tile": list(tile), "heads": Hh,
                    "head_dim": D, "batch": B, "window": list(wins[0]),
-                   "step": "reorder q,k,v + sta_forward + unreorder o",
+                   "step": "sta_forward_raster: tile reorder of q,k,v and unreorder of o inside the "
+                           "forward kernel's loads and stores (one launch)",
                    "pct_of_peak_step": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "sta_forward (fwd_bf16_kernel)",
+                     "traffic": traffic, "kernel": "sta_forward_raster (fwd_bf16_kernel, raster instance)",
                      "kernel_ms": round(fwd_ms, 4), "flops_per_launch": flops},
     }
 
@@ -221,6 +226,26 @@ def main():
 
     if not args.no_legs:
         legs = {}
+        # the same step with separate reorder kernels (and the tile-major
+        # tensors the dense leg uses)
+        def reorder_step(t_step, t_fwd):
+            with t_step:
+                sta.tile_reorder(q, latent, tile, out=qt)
+                sta.tile_reorder(k, latent, tile, out=kt)
+                sta.tile_reorder(v, latent, tile, out=vt)
+                with t_fwd:
+                    sta.forward(qt, kt, vt, latent, tile, wins, out=ot, lse=lse)
+                sta.tile_unreorder(ot, latent, tile, out=o)
+        reorder_step(Timer(torch), Timer(torch))
+        rt_step, rt_fwd = Timer(torch), Timer(torch)
+        for _ in range(5):
+            reorder_step(rt_step, rt_fwd)
+        torch.cuda.synchronize()
+        legs["step_with_reorder_kernels"] = {
+            "ms": round(rt_step.total_ms() / 5, 3), "tflops": round(flops / (rt_step.total_ms() / 5) / 1e9, 1),
+            "sta_forward_ms": round(rt_fwd.total_ms() / 5, 3),
+            "sta_forward_tflops": round(flops / (rt_fwd.total_ms() / 5) / 1e9, 1),
+            "note": "reorder q,k,v + sta_forward (tile-major) + unreorder o, five launches"}
         # dense denominator on the same tensors
         dense_t = Timer(torch)
         sta.dense_forward(qt, kt, vt, out=o, want_lse=False)

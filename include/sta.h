@@ -124,6 +124,19 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
                 float scale, sta_dtype dt, void* stream);
 
+/* STA forward on raster-order tensors: the tile reorder of q, k, v and the
+ * unreorder of o (and lse) folded into the kernel's own loads and stores, so
+ * one launch replaces reorder x3 + sta_forward + unreorder with the same
+ * arithmetic in the same order (outputs bit-identical to that sequence).
+ * q, k, v, o: bf16 [B, Hh, T*H*W, D] in raster order (W fastest); lse: fp32
+ * [B, Hh, T*H*W] raster or NULL.  Needs a whole-tile latent
+ * (STA_ERR_NOT_TILE_MULTIPLE otherwise; use the reorder path for padding),
+ * STA_BF16 with D in {64, 128}, L % 32 == 0 and the tile width a multiple of
+ * 512 / D (STA_ERR_UNSUPPORTED otherwise).  Other arguments as sta_forward. */
+int sta_forward_raster(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                       const int32_t* win_host, float scale, sta_dtype dt, void* stream);
+
 /* Bytes of device workspace sta_backward needs: 8*B*Hh*S' for per-row
  * statistics (fp32 Dl and LSE*log2(e)) plus, for STA_BF16, 4*Hh*n0*n1*n2 for a
  * per-head order of the key tiles.  0 for invalid sizes. */

@@ -34,6 +34,8 @@ SIGNATURES = {
     "sta_tile_pairs_host": (ctypes.c_int, [c_vp, c_vp, Dim3, Dim3, c_vp, c_i64, ctypes.c_int]),
     "sta_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
                                    c_f32, ctypes.c_int, c_vp]),
+    "sta_forward_raster": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3,
+                                          c_vp, c_f32, ctypes.c_int, c_vp]),
     "sta_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int]),
     "sta_backward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                     c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
@@ -215,6 +217,27 @@ def forward(q, k, v, latent, tile, windows, scale=None, out=None, lse=None, want
     _check(lib().sta_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, D,
                              _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale, _dtype(q),
                              _stream(q)), "sta_forward")
+    return out, lse
+
+
+def forward_raster(q, k, v, latent, tile, windows, scale=None, out=None, lse=None, want_lse=True):
+    """STA forward on raster-order [B, Hh, T*H*W, D] tensors (reorder and
+    unreorder inside the kernel): returns (O, LSE or None), both raster."""
+    B, Hh, S, D = _shape4(q, "q")
+    if S != raster_len(latent):
+        raise ValueError(f"q has {S} rows, the latent {latent} has {raster_len(latent)} tokens")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    w = _windows(windows, Hh)
+    out = torch.empty_like(q) if out is None else out
+    _same(q.shape, "q", ("q", q), ("k", k), ("v", v), ("out", out))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hh, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, Hh, S) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, Hh, S]")
+    lp = _dev(lse, "lse") if lse is not None else c_vp(None)
+    _check(lib().sta_forward_raster(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), lp, B, Hh, D,
+                                    _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale, _dtype(q),
+                                    _stream(q)), "sta_forward_raster")
     return out, lse
 
 

@@ -205,6 +205,26 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
   return forward_impl(q, k, v, o, lse, B, Hh, D, g, ht, scale, dt, stream);
 }
 
+int sta_forward_raster(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                       const int32_t* win_host, float scale, sta_dtype dt, void* stream) {
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  if (!q || !k || !v || !o) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
+  if ((st = check_sizes(B, Hh, D, g))) return st;
+  if (g.padded) return STA_ERR_NOT_TILE_MULTIPLE;
+  if (dt != STA_BF16 || !fwd_raster_supported((int)D, g)) return STA_ERR_UNSUPPORTED;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return STA_ERR_ALIGN;
+  return to_status(launch_fwd_bf16_raster((const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)v, (uint16_t*)o, lse, g, ht, (int)B,
+                                          (int)Hh, (int)D, scale, (hipStream_t)stream));
+}
+
 size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,
                                     sta_dim3 tile, sta_dtype dt) {
   (void)D;

@@ -142,8 +142,21 @@ __device__ __forceinline__ void pv_stage(const bf16x8 (&vf)[D / 32][2], const bf
       for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma32(vf[dt][s], pf[qt][s], oacc[qt][dt]);
 }
 
+// Raster row (inside its sequence) of intra-tile position r of tile
+// (a0, a1, a2): the tile-major -> raster map of the reorder, for one row.
+__device__ __forceinline__ uint32_t raster_row(int a0, int a1, int a2, uint32_t r,
+                                               const Geometry& g) {
+  const uint32_t i0 = fdiv(r, g.fhw), rem = r - i0 * (uint32_t)(g.h * g.w);
+  const uint32_t i1 = fdiv(rem, g.fw), i2 = rem - i1 * (uint32_t)g.w;
+  return ((uint32_t)(a0 * g.t) + i0) * (uint32_t)g.H * (uint32_t)g.W +
+         ((uint32_t)(a1 * g.h) + i1) * (uint32_t)g.W + (uint32_t)(a2 * g.w) + i2;
+}
+
 // LSE_ONLY: the log-sum-exp alone (v and o unused): K blocks only, no P V.
-template <int D, int QT, int NW, int OCC, bool LSE_ONLY>
+// RASTER: q, k, v, o and lse are in raster order (a latent of whole tiles
+// whose tile width is a multiple of a copy segment's rows): the reorder and
+// unreorder happen in the kernel's own loads and stores.
+template <int D, int QT, int NW, int OCC, bool LSE_ONLY, bool RASTER>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, Geometry g,
@@ -194,18 +207,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   const uint16_t* kb = k + seq * D;
   const uint16_t* vb = v + seq * D;
 
+  // Window of this query tile.
+  const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
+
   // Q^T fragments (B operand): lane holds 8 consecutive d of its query row.
+  // qrow[qt]: the lane's query row inside the sequence (tile-major, or its
+  // raster position).
   const int qrow0 = qtile * g.L + sub * C::ROWS + wave * QT * 32;
+  uint32_t qrow[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int tm = qrow0 + qt * 32 + c32;
+    qrow[qt] = RASTER ? raster_row(a0, a1, a2, (uint32_t)(tm - qtile * g.L), g) : (uint32_t)tm;
+  }
   bf16x8 qf[QT][C::KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      qf[qt][ks] = as_bf16x8(
-          *(const u32x4*)(q + (seq + qrow0 + qt * 32 + c32) * D + ks * 16 + grp * 8));
-
-  // Window of this query tile.
-  const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
+      qf[qt][ks] =
+          as_bf16x8(*(const u32x4*)(q + (seq + qrow[qt]) * D + ks * 16 + grp * 8));
   const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
   const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
             s2 = window_start(a2, w2, g.n2);
@@ -229,8 +250,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   };
   const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
   auto issue = [&](char* kl, char* vl) {
-    if constexpr (LSE_ONLY) copier.issue_k(kb, (size_t)next_key0(), kl);
-    else copier.issue(kb, vb, (size_t)next_key0(), kl, vl);
+    if constexpr (LSE_ONLY) {
+      copier.issue_k(kb, (size_t)next_key0(), kl);
+    } else if constexpr (RASTER) {
+      // raster rows of this block's segments (scalar: the same in every lane)
+      using Cp = KvDma<D, KB, NW>;
+      uint32_t rows[Cp::PT];
+#pragma unroll
+      for (int e = 0; e < Cp::PT; ++e)
+        rows[e] = raster_row(s0 + i0, s1 + i1, s2 + i2,
+                             (uint32_t)(jb * KB + (copier.wave_u + e * NW) * Cp::RPS), g);
+      next_key0();
+      copier.issue_rows(kb, vb, rows, kl, vl);
+    } else {
+      copier.issue(kb, vb, (size_t)next_key0(), kl, vl);
+    }
   };
 
   // Padded latents: keys at padding positions of a partial key tile are masked
@@ -373,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const int rin = qrow0 - qtile * g.L + qt * 32 + c32;  // row inside the query tile
     const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
     const float inv = real ? 1.0f / lt : 0.0f;
-    const size_t row = seq + qrow0 + qt * 32 + c32;
+    const size_t row = seq + qrow[qt];
     if constexpr (!LSE_ONLY) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
@@ -398,7 +432,7 @@ inline int xcd_group_items(int seqs, int items_per_seq) {
   return 0;
 }
 
-template <int D, int QT, int NW, int OCC, bool LSE_ONLY = false>
+template <int D, int QT, int NW, int OCC, bool LSE_ONLY = false, bool RASTER = false>
 hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                       float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                       float scale, hipStream_t st) {
@@ -406,7 +440,7 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
   const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, LSE_ONLY>), dim3((uint32_t)total),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, LSE_ONLY, RASTER>), dim3((uint32_t)total),
                      dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, B, Hh, scale * kLog2e, bpt,
                      total, group);
   return hipGetLastError();
@@ -416,21 +450,44 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
 
 bool fwd_bf16_supported(int D, int L) { return (D == 64 || D == 128) && L % 32 == 0; }
 
+template <bool RASTER>
+hipError_t launch_fwd_order(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                            float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
+                            int D, float scale, hipStream_t st) {
+  const int L = g.L;
+  if (D == 128) {
+    if (L % 128 == 0)
+      return launch_cfg<128, 1, 4, 2, false, RASTER>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    if (L % 64 == 0)
+      return launch_cfg<128, 1, 2, 2, false, RASTER>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<128, 1, 1, 1, false, RASTER>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+  }
+  if (D == 64) {
+    if (L % 128 == 0)
+      return launch_cfg<64, 1, 4, 2, false, RASTER>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    if (L % 64 == 0)
+      return launch_cfg<64, 1, 2, 2, false, RASTER>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+    return launch_cfg<64, 1, 1, 1, false, RASTER>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                            int D, float scale, hipStream_t st) {
-  const int L = g.L;
-  if (D == 128) {
-    if (L % 128 == 0) return launch_cfg<128, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    if (L % 64 == 0) return launch_cfg<128, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<128, 1, 1, 1>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-  }
-  if (D == 64) {
-    if (L % 128 == 0) return launch_cfg<64, 1, 4, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    if (L % 64 == 0) return launch_cfg<64, 1, 2, 2>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<64, 1, 1, 1>(q, k, v, o, lse, g, ht, B, Hh, scale, st);
-  }
-  return hipErrorInvalidValue;
+  return launch_fwd_order<false>(q, k, v, o, lse, g, ht, B, Hh, D, scale, st);
+}
+
+bool fwd_raster_supported(int D, const Geometry& g) {
+  // a copy segment (1 KiB) holds 1024 / (2 D) rows; they must be consecutive
+  // raster rows, so the tile width must be a multiple of that count
+  return fwd_bf16_supported(D, g.L) && !g.padded && g.w % (512 / D) == 0;
+}
+
+hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  uint16_t* o, float* lse, const Geometry& g, const HeadTable& ht,
+                                  int B, int Hh, int D, float scale, hipStream_t st) {
+  return launch_fwd_order<true>(q, k, v, o, lse, g, ht, B, Hh, D, scale, st);
 }
 
 hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, const Geometry& g,

@@ -28,6 +28,13 @@ bool fwd_bf16_supported(int D, int L);
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                            int D, float scale, hipStream_t stream);
+// The same forward on raster-order q, k, v, o and lse (the reorder folded into
+// the kernel's loads and stores): whole-tile latents whose tile width is a
+// multiple of 512 / D rows.
+bool fwd_raster_supported(int D, const Geometry& g);
+hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  uint16_t* o, float* lse, const Geometry& g, const HeadTable& ht,
+                                  int B, int Hh, int D, float scale, hipStream_t stream);
 // The forward's log-sum-exp alone (no P V, V not read).
 hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, const Geometry& g,
                            const HeadTable& ht, int B, int Hh, int D, float scale, hipStream_t stream);

@@ -193,6 +193,22 @@ struct KvDma {
       dma16(vbase + goff[e], vl + seg * 1024);
     }
   }
+  // The same block gathered from a raster-order sequence: seg_row[e] is the
+  // raster row of the first of the RPS rows of segment wave + e * NW (those
+  // rows must be consecutive in raster order).
+  __device__ __forceinline__ void issue_rows(const uint16_t* kg, const uint16_t* vg,
+                                             const uint32_t (&seg_row)[PT], char* kl,
+                                             char* vl) const {
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+      const int seg = wave_u + e * NW;
+      // goff[e] counts from the block's first row; the lane's offset inside
+      // its segment drops the segment's first seg * RPS rows.
+      const uint32_t in_seg = goff[e] - (uint32_t)(seg * RPS * D * 2);
+      dma16((const char*)(kg + (size_t)seg_row[e] * D) + in_seg, kl + seg * 1024);
+      dma16((const char*)(vg + (size_t)seg_row[e] * D) + in_seg, vl + seg * 1024);
+    }
+  }
   // The K block alone (PT copies per wave).
   __device__ __forceinline__ void issue_k(const uint16_t* kg, size_t row0, char* kl) const {
     const char* kbase = (const char*)(kg + row0 * D);

@@ -89,6 +89,22 @@ def test_forward_argument_errors(lib):
     assert lib.sta_forward(P, P, P, P, NUL, 1, 2, 128, d3(6, 16, 16), d3(2, 4, 4), NUL, 0.1, 0, NUL) == ARG
 
 
+def test_forward_raster_argument_errors(lib):
+    w = win([(3, 3, 3), (3, 3, 3)])
+
+    def fr(latent=(6, 16, 32), tile=(2, 4, 8), D=128, dt=L.STA_BF16, q=P, lse=NUL):
+        return lib.sta_forward_raster(q, P, P, P, lse, 1, 2, D, d3(*latent), d3(*tile),
+                                      w.ctypes.data_as(ctypes.c_void_p), 0.1, dt, NUL)
+    assert fr(q=NUL) == ARG
+    assert fr(latent=(5, 16, 32)) == NOT_MULT                 # padding needs the reorder path
+    assert fr(dt=L.STA_F32) == UNSUP
+    assert fr(tile=(2, 8, 2), latent=(6, 16, 32)) == UNSUP    # copy segments of 4 rows span x-runs
+    assert fr(D=64, tile=(2, 8, 4)) == UNSUP                   # D = 64: 8-row segments, width 4 too narrow
+    assert fr(D=96) == UNSUP
+    assert fr(q=MIS) == ALIGN
+    assert fr(lse=MIS) == ALIGN
+
+
 def test_reorder_argument_errors(lib):
     f = lib.sta_tile_reorder
     assert f(NUL, P, 1, 2, 64, d3(6, 16, 16), d3(2, 4, 4), 0, NUL) == ARG

@@ -122,6 +122,52 @@ def test_backward_f32_tiny(sta):
 
 # ------------------------------------------------------------------ forward, bf16 MFMA
 
+RASTER_CASES = [  # latent, tile, B, windows, D: every workgroup shape of the raster instance
+    ((6, 32, 32), (2, 8, 8), 2, [(3, 3, 3), (1, 4, 2)], 128),     # L = 128: four waves
+    ((6, 16, 32), (2, 4, 8), 1, [(3, 3, 3), (1, 2, 3)], 128),     # L = 64: two waves
+    ((12, 16, 24), (3, 4, 8), 1, [(3, 3, 3), (2, 1, 2)], 128),    # L = 96: one wave
+    ((6, 32, 32), (2, 8, 8), 1, [(3, 3, 3), (2, 2, 2)], 64),      # D = 64 (8-row copy segments)
+    ((1, 32, 40), (1, 8, 8), 2, [(1, 3, 3), (1, 1, 5)], 128),     # 2D
+]
+
+
+@pytest.mark.parametrize("latent,tile,B,wins,D", RASTER_CASES)
+def test_forward_raster_matches_oracle_and_reorder_path(sta, latent, tile, B, wins, D):
+    """Raster-order forward: within tolerance of the oracle in raster order, and
+    bit-identical to reorder -> sta_forward -> unreorder."""
+    S = int(np.prod(latent))
+    x = I.make_inputs(B, len(wins), S, D, "bf16", seed=9)
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sta.forward_raster(q, k, v, latent, tile, wins)
+    ro, rl = O.forward(to64(x["q"]), to64(x["k"]), to64(x["v"]), latent, tile, wins, D ** -0.5,
+                       order="raster")
+    eo, el = err_report(to64(o), ro), err_report(to64(lse), rl)
+    print("O", eo, "LSE", el)
+    assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+    assert el["max_abs"] < BF16_TOL
+    qt, kt, vt = (sta.tile_reorder(a, latent, tile) for a in (q, k, v))
+    ot, lt = sta.forward(qt, kt, vt, latent, tile, wins)
+    assert torch.equal(sta.tile_unreorder(ot, latent, tile).view(torch.int16), o.view(torch.int16))
+    lr = sta.tile_unreorder(lt.unsqueeze(-1), latent, tile).squeeze(-1)
+    assert torch.equal(lr.view(torch.int32), lse.view(torch.int32))
+
+
+def test_forward_raster_hunyuan_bit_identical(sta):
+    """(30,48,80), tile (6,8,8), 24 heads, mixed windows: the raster instance
+    equals reorder -> sta_forward -> unreorder bit for bit."""
+    w = I.WORKLOADS["hunyuan_30x48x80_mixed"]
+    latent, tile, wins = w["latent"], w["tile"], w["windows"]
+    S = int(np.prod(latent))
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q, k, v = (torch.randn((1, 24, S, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    o, lse = sta.forward_raster(q, k, v, latent, tile, wins)
+    qt, kt, vt = (sta.tile_reorder(a, latent, tile) for a in (q, k, v))
+    ot, lt = sta.forward(qt, kt, vt, latent, tile, wins)
+    assert torch.equal(sta.tile_unreorder(ot, latent, tile).view(torch.int16), o.view(torch.int16))
+    lr = sta.tile_unreorder(lt.unsqueeze(-1), latent, tile).squeeze(-1)
+    assert torch.equal(lr.view(torch.int32), lse.view(torch.int32))
+
+
 BF16_SMALL = [  # latent, tile, B, windows, D   (tile volume 32 and 128; several tiles; batch 2)
     ((6, 16, 16), (2, 4, 4), 2, [(3, 3, 3), (1, 2, 5), (9, 9, 9)], 128),
     ((6, 16, 16), (2, 4, 4), 1, [(2, 3, 1), (3, 1, 3)], 64),
