@@ -65,7 +65,7 @@ typedef enum { STA_BF16 = 0, STA_F32 = 1 } sta_dtype;
 enum {
   STA_OK = 0,
   STA_ERR_ARG = -1,               /* null pointer, non-positive size, bad scale */
-  STA_ERR_NOT_TILE_MULTIPLE = -2, /* unused since padding with masking is supported */
+  STA_ERR_NOT_TILE_MULTIPLE = -2, /* sta_forward_raster only: the other calls pad with masking */
   STA_ERR_WINDOW = -3,            /* a window entry < 1 */
   STA_ERR_UNSUPPORTED = -4,       /* head_dim, tile volume or dtype not built */
   STA_ERR_ALIGN = -5,             /* a tensor pointer not 16-byte aligned */
