@@ -343,6 +343,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   __shared__ __attribute__((aligned(1024))) char dol1[TB];
   __shared__ __attribute__((aligned(256))) char st0[256];
   __shared__ __attribute__((aligned(256))) char st1[256];
+  // dK: the workgroup's V rows stay in LDS (one 32-row tile per wave) rather
+  // than in registers, which keeps the kernel at two waves per SIMD.
+  __shared__ __attribute__((aligned(1024))) char vres[MODE == 1 ? NW * TB : 16];
 
   const KeyItem it = key_major_item(rank_tab, g, ht, B, Hh, blocks_per_tile);
   const int sub = it.sub, ktile = it.ktile, b = it.b, head = it.head;
@@ -353,14 +356,23 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   const uint16_t* qb = q + seq * D;
   const uint16_t* db = dout + seq * D;
 
-  // Resident key rows: K^T (and V^T for dK) as B operands (lane holds 8 d of key c32).
+  // Resident key rows: K^T as the B operand (lane holds 8 d of key c32); for
+  // dK the wave's 32 V rows are copied into its LDS tile (swizzled like the
+  // staged tiles) and read back per stage.
   const size_t krow0 = seq + (size_t)ktile * g.L + sub * (NW * 32) + wave * 32;
-  bf16x8 kf[KS], vf[MODE == 1 ? KS : 1];
+  bf16x8 kf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < KS; ++ks)
     kf[ks] = as_bf16x8(*(const u32x4*)(k + (krow0 + c32) * D + ks * 16 + grp * 8));
-    if constexpr (MODE == 1)
-      vf[ks] = as_bf16x8(*(const u32x4*)(v + (krow0 + c32) * D + ks * 16 + grp * 8));
+  char* vtile = vres + (MODE == 1 ? wave * TB : 0);
+  if constexpr (MODE == 1) {
+    constexpr int RPS = 1024 / (D * 2), CPR = D / 8;
+    const int rin = lane / CPR, p = lane % CPR;
+#pragma unroll
+    for (int seg = 0; seg < 32 / RPS; ++seg) {
+      const int r = seg * RPS + rin;
+      dma16(v + (krow0 + r) * D + ((p ^ (int)swz<D>(r)) * 8), vtile + seg * 1024);
+    }
   }
 
   // Query tiles whose window holds this key tile: a box [lo, hi] per dimension.
@@ -425,8 +437,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
       s = contract_rows<D>(qa, kf);   // S[q][key]
     }
     if constexpr (MODE == 1) {
-      bf16x8 da[KS];
+      bf16x8 da[KS], vf[KS];
       read_rows<D>(dol, da, grp, c32);
+      read_rows<D>(vtile, vf, grp, c32);
       dp = contract_rows<D>(da, vf);  // dP[q][key]
     }
     // lane's queries: 8i + 4g + jj; the A operand is P^T (MODE 0) or dS^T.
@@ -443,7 +456,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
         af[e >> 3][e & 7] = MODE == 0 ? (__bf16)p : (__bf16)(p * (dp[e] - d4[jj]));
       }
     }
-    // B operand: dO^T (MODE 0) or Q^T, read transposed from the staged tile.
+    // B operand: dO^T (MODE 0) or Q^T, read transposed from the staged tile
+    // (for dK, not hoisted above the vector work: registers are short).
+    if constexpr (MODE == 1) __builtin_amdgcn_sched_barrier(0);
     bf16x8 bt[DT][2];
     read_cols<D>(MODE == 0 ? dol : ql, bt, lane);
 #pragma unroll
@@ -514,7 +529,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                      dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, 2>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
                      k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
+  // dK fits two waves per SIMD in 4-wave workgroups; smaller ones keep one.
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, NW >= 4 ? 2 : 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
                      k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
   return hipGetLastError();
 }
