@@ -154,22 +154,21 @@ __device__ __forceinline__ f32x16 contract_rows(const bf16x8 (&a)[D / 16], const
 // --------------------------------------------------------------------------
 // 2. dQ (query-major).  Workgroup = NW waves x 32 query rows of one tile.
 // --------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
+template <int D, int NW, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dq,
     Geometry g, HeadTable ht, int B, int Hh, float c_log2, float scale, int blocks_per_tile,
     int total, int group_items) {
   constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2;
+  // Two-slot K/V ring plus a per-wave tile holding the wave's dO rows (64 KB
+  // per 4-wave workgroup, so two fit a CU at two waves per SIMD).
   __shared__ __attribute__((aligned(1024))) char kl0[TB];
   __shared__ __attribute__((aligned(1024))) char vl0[TB];
   __shared__ __attribute__((aligned(1024))) char kl1[TB];
   __shared__ __attribute__((aligned(1024))) char vl1[TB];
-  __shared__ __attribute__((aligned(1024))) char kl2[TB];
-  __shared__ __attribute__((aligned(1024))) char vl2[TB];
-  __shared__ __attribute__((aligned(1024))) char kl3[TB];
-  __shared__ __attribute__((aligned(1024))) char vl3[TB];
+  __shared__ __attribute__((aligned(1024))) char dores[NW * TB];
 
   uint32_t item = work_item(total, group_items);
   const int sub = item % blocks_per_tile;
@@ -185,12 +184,22 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
   const uint16_t* kb = k + seq * D;
   const uint16_t* vb = v + seq * D;
 
-  const size_t row = seq + (size_t)qtile * g.L + sub * (NW * 32) + wave * 32 + c32;
-  bf16x8 qf[KS], dof[KS];
+  const size_t row0 = seq + (size_t)qtile * g.L + sub * (NW * 32) + wave * 32;
+  const size_t row = row0 + c32;
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = as_bf16x8(*(const u32x4*)(q + row * D + ks * 16 + grp * 8));
-    dof[ks] = as_bf16x8(*(const u32x4*)(dout + row * D + ks * 16 + grp * 8));
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(q + row * D + ks * 16 + grp * 8));
+  // The wave's 32 dO rows go to its LDS tile (the staged tiles' swizzle) and
+  // are read back as the dP^T B operand each stage.
+  char* dotile = dores + wave * TB;
+  {
+    constexpr int RPS = 1024 / (D * 2), CPR = D / 8;
+    const int rin = lane / CPR, p = lane % CPR;
+#pragma unroll
+    for (int seg = 0; seg < 32 / RPS; ++seg) {
+      const int r = seg * RPS + rin;
+      dma16(dout + (row0 + r) * D + ((p ^ (int)swz<D>(r)) * 8), dotile + seg * 1024);
+    }
   }
   const float lrow = lse2[row], drow = dl[row];
 
@@ -253,7 +262,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
     read_rows<D>(vl, vr, grp, c32);
     f32x16 st = contract_rows<D>(kf, qf);         // S^T[key][q]
     mask_keys(st);
-    const f32x16 dpt = contract_rows<D>(vr, dof);  // dP^T[key][q]
+    f32x16 dpt;
+    {
+      bf16x8 dof[KS];
+      read_rows<D>(dotile, dof, grp, c32);
+      dpt = contract_rows<D>(vr, dof);              // dP^T[key][q]
+    }
     bf16x8 ds[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -270,31 +284,26 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(ktf[dt][s], ds[s], acc[dt]);
   };
 
-  // Four-stage LDS ring: stage j sits in buffer j % 4; its copy is issued
-  // three stages ahead, right after the barrier that ends stage j - 4.
+  // Two-stage LDS ring: stage j sits in slot j % 2; its copy is issued two
+  // stages ahead, right after the barrier that ends stage j - 2 (every wave
+  // has then finished reading that slot: each step consumes its reads).
   constexpr int PER = dma_kv_per_wave<D, kStage, NW>();
   issue(kl0, vl0);
   if (nst > 1) issue(kl1, vl1);
-  if (nst > 2) issue(kl2, vl2);
-  if (nst > 3) issue(kl3, vl3);
-  wait_stage<PER>(nst - 1);
+  wait_stage<PER>(nst > 1 ? 1 : 0);   // the dO tile and stage 0 have landed
   barrier_lds();
   auto stage = [&](int j, const char* kl, const char* vl, char* kf_, char* vf_) {
     step(kl, vl);
     if (j + 1 < nst) {
-      wait_stage<PER>(nst - 2 - j);
+      wait_dma();
       barrier_lds();
-      if (j + 4 < nst) issue(kf_, vf_);
+      if (j + 2 < nst) issue(kf_, vf_);
     }
   };
-  for (int j = 0; j < nst; j += 4) {
+  for (int j = 0; j < nst; j += 2) {
     stage(j, kl0, vl0, kl0, vl0);
     if (j + 1 >= nst) break;
     stage(j + 1, kl1, vl1, kl1, vl1);
-    if (j + 2 >= nst) break;
-    stage(j + 2, kl2, vl2, kl2, vl2);
-    if (j + 3 >= nst) break;
-    stage(j + 3, kl3, vl3, kl3, vl3);
   }
 
   // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj; zero
@@ -525,7 +534,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   const int total = B * Hh * g.ntiles * bpt;
   const int group = group_items_for(B * Hh, g.ntiles * bpt);
   const float c_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
+  // dQ fits two waves per SIMD in 4-wave workgroups; smaller ones keep one.
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NW >= 4 ? 2 : 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
                      dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, 2>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
                      k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
