@@ -56,6 +56,12 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility: exactly the functions below
+ * are exported. */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
 typedef struct {
   int32_t t, h, w;
 } sta_dim3;
@@ -204,6 +210,10 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
  * Asynchronous on stream; time it with events. */
 int sta_calib_mfma_bf16(const void* operands, int64_t operand_bytes, int64_t iters, int64_t blocks,
                         float* out, void* stream);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,7 @@ SOURCES = ["api.hip", "reorder.hip", "f32_debug.hip", "fwd_bf16.hip", "bwd_bf16.
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -8,6 +8,8 @@ and no device memory is touched: the fake device pointers are never used.
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import torch
@@ -42,6 +44,15 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, f"binding lacks {n}"
+
+
+def test_exports_nothing_else(lib):
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if ln.split()[1:2] == ["T"]})
+    assert exported == header_functions()
 
 
 def test_strerror_covers_codes(lib):
