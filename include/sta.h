@@ -130,8 +130,10 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
                 float scale, sta_dtype dt, void* stream);
 
-/* STA forward on raster-order tensors: the tile reorder of q, k, v and the
- * unreorder of o (and lse) folded into the kernel's own loads and stores, so
+/* STA forward on raster-order tensors ([STA-abs] attention over the tile
+ * window, with [STA-meth]'s tile-contiguous order used only inside the
+ * kernel): the tile reorder of q, k, v and the unreorder of o (and lse)
+ * folded into the kernel's own loads and stores, so
  * one launch replaces reorder x3 + sta_forward + unreorder with the same
  * arithmetic in the same order (outputs bit-identical to that sequence).
  * q, k, v, o: bf16 [B, Hh, T*H*W, D] in raster order (W fastest); lse: fp32
