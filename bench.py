@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-FWD_SRC = os.path.join(ROOT, "sparse_sliding_tile_amd", "csrc", "fwd_bf16.hip")
+FWD_SOURCES = [os.path.join(ROOT, "sparse_sliding_tile_amd", "csrc", f)
+               for f in ("fwd_bf16.hip", "mfma_common.h", "sta_common.h", "kernels.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sta_forward_hunyuan_30x48x80_traffic.txt")
 
 
@@ -83,9 +84,17 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in self.pairs)
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths=None):
+    """Hash of the forward kernel's code: its source and the headers it uses,
+    with comments and blank lines dropped (a comment edit is no kernel change)."""
+    h = hashlib.sha256()
+    for path in paths or FWD_SOURCES:
+        with open(path) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -98,7 +107,7 @@ def read_traffic():
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     vals[k.strip()] = v.strip()
-        if vals.get("source_sha256_16") != source_hash(FWD_SRC):
+        if vals.get("source_sha256_16") != source_hash():
             return None
         return float(vals["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

@@ -2,14 +2,20 @@
 //
 // "Sliding Tile Attention" (arXiv 2502.04507 summary page, abstract and method
 // details): each query tile attends densely to the key tiles of its window, so
-// every (query block, key block) product below is a full dense contraction and
-// there is no mask anywhere in the inner loop.
+// every (query block, key block) product below is a full dense contraction.
+// The only mask is the padding one of latents that are not a whole number of
+// tiles (OpenReview rebuttal, answer on input resolution), applied to the key
+// blocks of partial tiles only.
 //
 // Work decomposition
 //   One workgroup = NW waves = NW*QT*32 query rows of one query tile of one
 //   (batch, head).  Each wave keeps its QT*32 query rows resident in registers
 //   for the whole key walk.  The key tiles of the window are walked in KB-key
-//   blocks, double-buffered in LDS and filled by 16-byte global->LDS DMA.
+//   blocks through a ring of LDS slots filled by 16-byte global->LDS DMA.
+// Instances: tile-major tensors (sta_forward, sta_dense_forward), raster-order
+//   tensors with the reorder folded into the loads and stores
+//   (sta_forward_raster), and the normaliser (log-sum-exp) alone, K only and
+//   no P V (sta_window_mass).
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16)
 //   S^T = K Q^T     A = K rows (LDS), B = Q^T (registers).  Lane l of the
