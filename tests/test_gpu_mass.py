@@ -89,3 +89,18 @@ def test_window_mass_hunyuan_shape_sampled_and_closed_forms(sta):
     m0 = to64(sta.window_mass(z, k, latent, tile, cands, workspace=ws))[:, 0, :]
     share = np.array([np.prod([min(w, m) for w, m in zip(c, n)]) * L / S for c in cands])
     assert np.abs(m0 - share[:, None]).max() < 1e-5
+
+
+def test_calibration_loop_closed_form(sta):
+    """The matrix-core calibration loop on all-ones bf16 operands: each of the
+    four accumulator chains takes 4 MFMAs of 16 ones per iteration, so every
+    thread's sum over its 4 x 16 accumulator elements is 4096 * iters."""
+    ops = torch.ones(1 << 12, dtype=torch.bfloat16, device="cuda")
+    out, flop = sta.calib_mfma_bf16(ops, 10, 8)
+    torch.cuda.synchronize()
+    assert flop == 8 * 4 * 10 * 16 * 32768
+    assert torch.equal(out, torch.full_like(out, 4096.0 * 10))
+    zeros = torch.zeros(1 << 12, dtype=torch.bfloat16, device="cuda")
+    out0, _ = sta.calib_mfma_bf16(zeros, 10, 8)
+    torch.cuda.synchronize()
+    assert not out0.any()
