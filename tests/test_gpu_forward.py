@@ -300,3 +300,25 @@ def test_dense_f32_small(sta):
     ro, rl = O.dense_forward(to64(x["q"]), to64(x["k"]), to64(x["v"]), 0.125)
     assert err_report(to64(o), ro)["max_abs"] < F32_TOL
     assert err_report(to64(lse), rl)["max_abs"] < F32_TOL
+
+
+def test_forward_bf16_finetune_sampled(sta):
+    """The fine-tuning shape (24,64,64), tile (6,8,8), window (3,5,5): forward
+    O and LSE on sampled query tiles (its backward is checked elsewhere)."""
+    _check_sampled(sta, "finetune_24x64x64_w355", heads=[0, 23])
+
+
+def test_dense_bf16_hunyuan_sampled(sta):
+    """Dense attention (the speedup denominator) at the HunyuanVideo sequence
+    length S = 115200, 2 heads, on sampled rows against all keys."""
+    S = 30 * 48 * 80
+    g = torch.Generator(device="cuda").manual_seed(31)
+    q, k, v = (torch.randn((1, 2, S, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    o, lse = sta.dense_forward(q, k, v, scale=128 ** -0.5)
+    rows = np.concatenate([np.arange(0, 48), np.arange(S // 2, S // 2 + 48), np.arange(S - 48, S)])
+    rt = torch.from_numpy(rows).cuda()
+    ro, rl = O.dense_forward(to64(q), to64(k), to64(v), 128 ** -0.5, rows=rows)
+    eo, el = err_report(to64(o[:, :, rt]), ro), err_report(to64(lse[:, :, rt]), rl)
+    print("dense O", eo, "LSE", el)
+    assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+    assert el["max_abs"] < BF16_TOL
