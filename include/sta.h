@@ -81,6 +81,7 @@ enum {
 };
 
 #define STA_MAX_HEADS 256
+#define STA_MAX_CANDIDATES 8 /* candidate windows per sta_window_mass call */
 
 /* Human-readable text for a return code (static storage). */
 const char* sta_strerror(int code);
@@ -172,8 +173,10 @@ int sta_dense_forward(const void* q, const void* k, const void* v, void* o, floa
                       int64_t Hh, int64_t S, int64_t D, float scale, sta_dtype dt, void* stream);
 
 /* Bytes of device workspace sta_window_mass needs: 8*B*Hh*S' (two fp32
- * log-sum-exp vectors over the tile-major rows).  0 for invalid sizes. */
-size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, sta_dim3 tile);
+ * log-sum-exp vectors over the tile-major rows) plus 4*n_cand*B*Hh*ceil(S'/32)
+ * (per-block partial sums).  0 for invalid sizes. */
+size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, sta_dim3 tile,
+                                       int64_t n_cand);
 
 /* Attention mass of candidate windows, the measurement side of the per-head
  * window search ([STA-meth]: each head gets its own window, configured
@@ -186,14 +189,16 @@ size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, s
  * its mean over the real query rows of (b, h) for window cand_host[c].
  * q, k: tile-major [B, Hh, S', D] of type dt (as for sta_forward; V is not
  * needed).  cand_host: host int32 [n_cand][3] windows in tiles, each >= 1,
- * clamped to the grid, the same for every head; read during the call.
+ * clamped to the grid, the same for every head; read during the call;
+ * 1 <= n_cand <= STA_MAX_CANDIDATES (STA_ERR_UNSUPPORTED above).
  * workspace: device memory of at least sta_window_mass_workspace_bytes(),
- * caller-owned, contents on entry irrelevant; on return it holds the per-row
- * statistics: fp32 [B, Hh, S'] LSE of the full window, then fp32 [B, Hh, S']
- * LSE of the last candidate (natural log, tile-major rows, 0 on padding
- * rows).  The work is one normaliser-only
- * forward pass with the full window plus one per candidate, each followed by a
- * per-(b, h) mean.  Errors as sta_forward, plus STA_ERR_WORKSPACE. */
+ * caller-owned, contents on entry irrelevant; on return it starts with the
+ * per-row statistics: fp32 [B, Hh, S'] LSE of the full window, then fp32
+ * [B, Hh, S'] LSE of the last candidate (natural log, tile-major rows, 0 on
+ * padding rows).  STA_BF16 does the work in one pass over the full window
+ * (Q K^T and the normaliser only; every candidate's share is summed under the
+ * shared running maximum), STA_F32 in one normaliser pass per window.
+ * Errors as sta_forward, plus STA_ERR_WORKSPACE. */
 int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, size_t ws_bytes,
                     int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
                     const int32_t* cand_host, int64_t n_cand, float scale, sta_dtype dt,

@@ -41,7 +41,7 @@ SIGNATURES = {
                                     c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
     "sta_dense_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
                                          c_f32, ctypes.c_int, c_vp]),
-    "sta_window_mass_workspace_bytes": (c_sz, [c_i64, c_i64, Dim3, Dim3]),
+    "sta_window_mass_workspace_bytes": (c_sz, [c_i64, c_i64, Dim3, Dim3, c_i64]),
     "sta_calib_mfma_bf16": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "sta_window_mass": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_sz, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
                                        c_i64, c_f32, ctypes.c_int, c_vp]),
@@ -281,8 +281,8 @@ def dense_forward(q, k, v, scale=None, out=None, want_lse=True):
     return out, lse
 
 
-def window_mass_workspace_bytes(B, Hh, latent, tile):
-    return int(lib().sta_window_mass_workspace_bytes(B, Hh, _dim3(latent), _dim3(tile)))
+def window_mass_workspace_bytes(B, Hh, latent, tile, n_cand):
+    return int(lib().sta_window_mass_workspace_bytes(B, Hh, _dim3(latent), _dim3(tile), int(n_cand)))
 
 
 def window_mass(q, k, latent, tile, candidates, scale=None, workspace=None, out=None):
@@ -295,7 +295,7 @@ def window_mass(q, k, latent, tile, candidates, scale=None, workspace=None, out=
     _same(q.shape, "q", ("q", q), ("k", k))
     scale = float(D) ** -0.5 if scale is None else float(scale)
     c = np.ascontiguousarray(np.asarray(candidates, dtype=np.int32).reshape(-1, 3))
-    nbytes = window_mass_workspace_bytes(B, Hh, latent, tile)
+    nbytes = window_mass_workspace_bytes(B, Hh, latent, tile, c.shape[0])
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     shape = (c.shape[0], B, Hh)

@@ -303,12 +303,16 @@ int sta_dense_forward(const void* q, const void* k, const void* v, void* o, floa
   return forward_impl(q, k, v, o, lse, B, Hh, D, g, ht, scale, dt, stream);
 }
 
-size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, sta_dim3 tile) {
+static_assert(STA_MAX_CANDIDATES == kMaxCandidates, "candidate limit");
+
+size_t sta_window_mass_workspace_bytes(int64_t B, int64_t Hh, sta_dim3 latent, sta_dim3 tile,
+                                       int64_t n_cand) {
   Geometry g;
-  if (B < 1 || Hh < 1 || make_geometry(latent, tile, &g) != STA_OK) return 0;
-  // Two fp32 log-sum-exp vectors over the tile-major rows: the full one and
-  // the candidate's.
-  return 2 * (size_t)B * Hh * (size_t)g.S * sizeof(float);
+  if (B < 1 || Hh < 1 || n_cand < 1 || make_geometry(latent, tile, &g) != STA_OK) return 0;
+  // Two fp32 log-sum-exp vectors over the tile-major rows (full window, last
+  // candidate), then one fp32 partial sum per (candidate, sequence, 32 rows).
+  const size_t rows = (size_t)B * Hh * (size_t)g.S;
+  return 2 * rows * sizeof(float) + (size_t)n_cand * B * Hh * ((g.S + 31) / 32) * sizeof(float);
 }
 
 int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, size_t ws_bytes,
@@ -321,8 +325,7 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
   if (!q || !k || !mass || !cand_host || n_cand < 1) return STA_ERR_ARG;
   if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
   if ((st = check_sizes(B, Hh, D, g))) return st;
-  if (Hh > STA_MAX_HEADS) return STA_ERR_UNSUPPORTED;
-  if (n_cand * B * Hh >= (1ll << 31)) return STA_ERR_TOO_LARGE;
+  if (Hh > STA_MAX_HEADS || n_cand > STA_MAX_CANDIDATES) return STA_ERR_UNSUPPORTED;
   if (dt == STA_BF16) {
     if (!fwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
   } else if (dt == STA_F32) {
@@ -330,7 +333,7 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
   } else {
     return STA_ERR_UNSUPPORTED;
   }
-  if (!workspace || ws_bytes < sta_window_mass_workspace_bytes(B, Hh, latent, tile))
+  if (!workspace || ws_bytes < sta_window_mass_workspace_bytes(B, Hh, latent, tile, n_cand))
     return STA_ERR_WORKSPACE;
   if (misaligned(q) || misaligned(k) || misaligned(workspace)) return STA_ERR_ALIGN;
   // Every table is built (and every window checked) before the first launch.
@@ -351,16 +354,26 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
   const hipStream_t s = (hipStream_t)stream;
   float* lse_full = (float*)workspace;
   float* lse_win = lse_full + (size_t)B * Hh * g.S;
-  auto lse_pass = [&](const HeadTable& ht, float* out) {
-    if (dt == STA_BF16)
-      return launch_lse_bf16((const uint16_t*)q, (const uint16_t*)k, out, g, ht, (int)B, (int)Hh,
-                             (int)D, scale, s);
-    return launch_fwd_f32((const float*)q, (const float*)k, (const float*)k, nullptr, out, g, ht,
-                          (int)B, (int)Hh, (int)D, scale, s);
-  };
-  hipError_t e = lse_pass(full, lse_full);
+  if (dt == STA_BF16) {
+    // one pass: the full window, every candidate's share under it
+    MassArgs ma{};
+    ma.partial = lse_win + (size_t)B * Hh * g.S;
+    ma.lse_last = lse_win;
+    ma.ncand = (int)n_cand;
+    for (int64_t c = 0; c < n_cand; ++c)
+      for (int d = 0; d < 3; ++d) ma.w[c][d] = cands[c].wp[0][d];  // clamped, same for all heads
+    hipError_t e = launch_mass_bf16((const uint16_t*)q, (const uint16_t*)k, lse_full, ma, g, full,
+                                    (int)B, (int)Hh, (int)D, scale, s);
+    if (e == hipSuccess) e = launch_mass_reduce(ma.partial, mass, g, (int)n_cand, B * Hh, s);
+    return to_status(e);
+  }
+  // fp32 debug path: a normaliser pass per window, then the mean of
+  // exp(LSE_win - LSE_full)
+  hipError_t e = launch_fwd_f32((const float*)q, (const float*)k, (const float*)k, nullptr,
+                                lse_full, g, full, (int)B, (int)Hh, (int)D, scale, s);
   for (int64_t c = 0; c < n_cand && e == hipSuccess; ++c) {
-    e = lse_pass(cands[c], lse_win);
+    e = launch_fwd_f32((const float*)q, (const float*)k, (const float*)k, nullptr, lse_win, g,
+                       cands[c], (int)B, (int)Hh, (int)D, scale, s);
     if (e == hipSuccess) e = launch_mass(lse_win, lse_full, mass + c * B * Hh, g, B * Hh, s);
   }
   return to_status(e);

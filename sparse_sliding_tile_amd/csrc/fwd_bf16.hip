@@ -113,11 +113,15 @@ __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (
   }
 }
 
-// Softmax normaliser only (no P V): running maximum and fp32 row sum of the
-// exponentials, with the same lazy rescale.
+// Softmax normaliser only (no P V), for the window mass: running maximum and
+// fp32 row sums of the exponentials, with the same lazy rescale.  The current
+// key tile's sum collects in ltile; at the tile's last block it joins the full
+// sum and the sums of the candidate windows that hold the tile (member bit c).
 template <int QT>
-__device__ __forceinline__ void lse_stage(const f32x16 (&sacc)[QT], float (&mrun)[QT],
-                                          float (&lrun)[QT], float c_log2) {
+__device__ __forceinline__ void mass_stage(const f32x16 (&sacc)[QT], float (&mrun)[QT],
+                                           float (&lfull)[QT], float (&ltile)[QT],
+                                           float (&lc)[QT][kMaxCandidates], int ncand,
+                                           bool tile_done, uint32_t member, float c_log2) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float mx = sacc[qt][0];
@@ -125,14 +129,25 @@ __device__ __forceinline__ void lse_stage(const f32x16 (&sacc)[QT], float (&mrun
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[qt][e]);
     const float mblk = xmax32(mx) * c_log2;
     if (mblk > mrun[qt] + kRescaleThreshold) {
-      lrun[qt] *= __builtin_amdgcn_exp2f(mrun[qt] - mblk);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mblk);
+      lfull[qt] *= alpha;
+      ltile[qt] *= alpha;
+#pragma unroll
+      for (int c = 0; c < kMaxCandidates; ++c) lc[qt][c] *= alpha;
       mrun[qt] = mblk;
     }
     const float mneg = -mrun[qt];
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ls += __builtin_amdgcn_exp2f(fmaf(sacc[qt][e], c_log2, mneg));
-    lrun[qt] += ls;
+    ltile[qt] += ls;
+    if (tile_done) {
+      lfull[qt] += ltile[qt];
+#pragma unroll
+      for (int c = 0; c < kMaxCandidates; ++c)
+        if (c < ncand && ((member >> c) & 1u)) lc[qt][c] += ltile[qt];
+      ltile[qt] = 0.f;
+    }
   }
 }
 
@@ -158,15 +173,17 @@ __device__ __forceinline__ uint32_t raster_row(int a0, int a1, int a2, uint32_t 
          ((uint32_t)(a1 * g.h) + i1) * (uint32_t)g.W + (uint32_t)(a2 * g.w) + i2;
 }
 
-// LSE_ONLY: the log-sum-exp alone (v and o unused): K blocks only, no P V.
+// MASS: the window mass (v and o unused): K blocks only, no P V; the head
+// table holds the full window and ma the candidate windows (see MassArgs).
 // RASTER: q, k, v, o and lse are in raster order (a latent of whole tiles
 // whose tile width is a multiple of a copy segment's rows): the reorder and
 // unreorder happen in the kernel's own loads and stores.
-template <int D, int QT, int NW, int OCC, bool LSE_ONLY, bool RASTER>
+template <int D, int QT, int NW, int OCC, bool MASS, bool RASTER>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, Geometry g,
-    HeadTable ht, int B, int Hh, float c_log2, int blocks_per_tile, int total, int group_items) {
+    HeadTable ht, MassArgs ma, int B, int Hh, float c_log2, int blocks_per_tile, int total,
+    int group_items) {
   using C = FwdCfg<D, QT, NW>;
   constexpr int KB = C::KB;
   // A ring of four stages, each buffer its own object so the compiler can
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   };
   const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
   auto issue = [&](char* kl, char* vl) {
-    if constexpr (LSE_ONLY) {
+    if constexpr (MASS) {
       copier.issue_k(kb, (size_t)next_key0(), kl);
     } else if constexpr (RASTER) {
       // raster rows of this block's segments (scalar: the same in every lane)
@@ -274,12 +291,30 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   };
 
   // Padded latents: keys at padding positions of a partial key tile are masked
-  // out of the stage being computed (a second walk over the key blocks).
+  // out of the stage being computed (a second walk over the key blocks).  The
+  // mass instance also reads off the walk whether the stage ends its key tile
+  // and which candidate windows hold that tile.
   int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  bool tile_done = false;
+  uint32_t member = 0;
   auto mask_keys = [&](f32x16 (&sacc)[QT]) {
-    if (!g.padded) return;
+    if (!MASS && !g.padded) return;
     const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
-    if (tile_partial(k0, k1, k2, g)) {
+    if constexpr (MASS) {
+      tile_done = cjb == bpt - 1;
+      member = 0;
+#pragma unroll
+      for (int c = 0; c < kMaxCandidates; ++c) {
+        if (c < ma.ncand) {
+          const int cw0 = ma.w[c][0], cw1 = ma.w[c][1], cw2 = ma.w[c][2];
+          const bool in = (unsigned)(k0 - window_start(a0, cw0, g.n0)) < (unsigned)cw0 &&
+                          (unsigned)(k1 - window_start(a1, cw1, g.n1)) < (unsigned)cw1 &&
+                          (unsigned)(k2 - window_start(a2, cw2, g.n2)) < (unsigned)cw2;
+          member |= (in ? 1u : 0u) << c;
+        }
+      }
+    }
+    if (g.padded && tile_partial(k0, k1, k2, g)) {
       const uint32_t m = block_real_mask(k0, k1, k2, cjb * KB, g, lane);
       if (m != 0xffffffffu) {  // blocks of a partial tile are often whole
         const uint32_t bits = lane_bits(m, lane);
@@ -304,12 +339,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
 
   f32x16 oacc[QT][C::DT];
   float mrun[QT], lrun[QT];
+  float ltile[QT], lcand[QT][kMaxCandidates];  // mass instance only
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] = f32x16{};
     mrun[qt] = -INFINITY;
     lrun[qt] = 0.f;
+    ltile[qt] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxCandidates; ++c) lcand[qt][c] = 0.f;
   }
 
   // Pipeline over 32-key stages; stage j sits in LDS slot j % SLOTS.  Four
@@ -325,7 +364,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // then P V of j, overlapping the reads.
   constexpr int SLOTS = NW >= 4 ? 4 : 2;
   constexpr int AHEAD = SLOTS == 4 ? 3 : 2;
-  constexpr int PER = LSE_ONLY ? KvDma<D, KB, NW>::PT : KvDma<D, KB, NW>::PER;
+  constexpr int PER = MASS ? KvDma<D, KB, NW>::PT : KvDma<D, KB, NW>::PER;
   issue(kl0, vl0);
   if (nblk > 1) issue(kl1, vl1);
   if constexpr (SLOTS == 4) {
@@ -350,15 +389,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // copy (reads behind the wave's own copy were measured slower).
   bf16x8 kf[C::KS], vfa[C::DT][2], vfb[C::DT][2];
   read_rows<D>(kl0, kf, grp, c32);
-  if constexpr (!LSE_ONLY) read_cols<D>(vl0, vfa, lane);
+  if constexpr (!MASS) read_cols<D>(vl0, vfa, lane);
 
   auto stage = [&](int j, bf16x8 (&vf)[C::DT][2], bf16x8 (&vf_nxt)[C::DT][2], const char* kl_nxt,
                    const char* vl_nxt, char* kl_far, char* vl_far) {
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
     mask_keys(sacc);
-    if constexpr (LSE_ONLY) {
-      lse_stage<QT>(sacc, mrun, lrun, c_log2);
+    if constexpr (MASS) {
+      mass_stage<QT>(sacc, mrun, lrun, ltile, lcand, ma.ncand, tile_done, member, c_log2);
       if (j + 1 < nblk) {
         wait_next(j);
         barrier_lds();
@@ -407,6 +446,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; zero on padding rows.
+  // Mass instance: row mass l_c / l per candidate, summed over the wave's 32
+  // rows into one partial per (candidate, sequence, 32-row block).
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float lt = xsum32(lrun[qt]);
@@ -414,7 +455,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
     const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow[qt];
-    if constexpr (!LSE_ONLY) {
+    if constexpr (!MASS) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -424,6 +465,23 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
           for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qt][dt][4 * i + j] * inv);
           *(bf16x4*)(o + row * D + dt * 32 + 8 * i + 4 * grp) = w;
         }
+    } else {
+      const size_t bh = (size_t)b * Hh + head;
+      const size_t nblk32 = (size_t)g.S / 32;
+      const size_t blk = (size_t)(qrow0 + qt * 32) / 32;
+#pragma unroll
+      for (int c = 0; c < kMaxCandidates; ++c) {
+        if (c < ma.ncand) {
+          const float lcs = xsum32(lcand[qt][c]);
+          float r = lcs * inv;  // 0 on padding rows
+          // sum over the 32 rows (lanes 0..31; lanes 32..63 hold the same rows)
+#pragma unroll
+          for (int off = 16; off > 0; off >>= 1) r += __shfl_xor(r, off, 32);
+          if (lane == 0) ma.partial[((size_t)c * B * Hh + bh) * nblk32 + blk] = r;
+          if (c == ma.ncand - 1 && ma.lse_last != nullptr && grp == 0)
+            ma.lse_last[row] = real ? (mrun[qt] + log2f(lcs)) * kLn2 : 0.0f;
+        }
+      }
     }
     if (lse != nullptr && grp == 0) lse[row] = real ? (mrun[qt] + log2f(lt)) * kLn2 : 0.0f;
   }
@@ -438,17 +496,17 @@ inline int xcd_group_items(int seqs, int items_per_seq) {
   return 0;
 }
 
-template <int D, int QT, int NW, int OCC, bool LSE_ONLY = false, bool RASTER = false>
+template <int D, int QT, int NW, int OCC, bool MASS = false, bool RASTER = false>
 hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                       float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
-                      float scale, hipStream_t st) {
+                      float scale, hipStream_t st, const MassArgs& ma = MassArgs{}) {
   using C = FwdCfg<D, QT, NW>;
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
   const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, LSE_ONLY, RASTER>), dim3((uint32_t)total),
-                     dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, B, Hh, scale * kLog2e, bpt,
-                     total, group);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER>), dim3((uint32_t)total),
+                     dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh, scale * kLog2e,
+                     bpt, total, group);
   return hipGetLastError();
 }
 
@@ -496,22 +554,24 @@ hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const ui
   return launch_fwd_order<true>(q, k, v, o, lse, g, ht, B, Hh, D, scale, st);
 }
 
-hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, const Geometry& g,
-                           const HeadTable& ht, int B, int Hh, int D, float scale, hipStream_t st) {
+hipError_t launch_mass_bf16(const uint16_t* q, const uint16_t* k, float* lse, const MassArgs& ma,
+                            const Geometry& g, const HeadTable& ht_full, int B, int Hh, int D,
+                            float scale, hipStream_t st) {
   const int L = g.L;
+  const HeadTable& ht = ht_full;
   if (D == 128) {
     if (L % 128 == 0)
-      return launch_cfg<128, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+      return launch_cfg<128, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st, ma);
     if (L % 64 == 0)
-      return launch_cfg<128, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<128, 1, 1, 1, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+      return launch_cfg<128, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st, ma);
+    return launch_cfg<128, 1, 1, 1, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st, ma);
   }
   if (D == 64) {
     if (L % 128 == 0)
-      return launch_cfg<64, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+      return launch_cfg<64, 1, 4, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st, ma);
     if (L % 64 == 0)
-      return launch_cfg<64, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
-    return launch_cfg<64, 1, 1, 1, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st);
+      return launch_cfg<64, 1, 2, 2, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st, ma);
+    return launch_cfg<64, 1, 1, 1, true>(q, k, k, nullptr, lse, g, ht, B, Hh, scale, st, ma);
   }
   return hipErrorInvalidValue;
 }

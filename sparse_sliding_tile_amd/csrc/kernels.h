@@ -35,9 +35,25 @@ bool fwd_raster_supported(int D, const Geometry& g);
 hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   uint16_t* o, float* lse, const Geometry& g, const HeadTable& ht,
                                   int B, int Hh, int D, float scale, hipStream_t stream);
-// The forward's log-sum-exp alone (no P V, V not read).
-hipError_t launch_lse_bf16(const uint16_t* q, const uint16_t* k, float* lse, const Geometry& g,
-                           const HeadTable& ht, int B, int Hh, int D, float scale, hipStream_t stream);
+// Window mass of up to kMaxCandidates candidate windows in one pass over the
+// full window (Q K^T and the softmax normaliser only, V not read): per query
+// row, the full normaliser l and, per candidate c, the part l_c of it whose
+// key tiles lie in window c, under one running maximum; l_c / l is the row's
+// mass.  Per-wave sums of the row masses go to partial[c][b*Hh+h][S/32],
+// LSE_full to lse, the last candidate's LSE to lse_last (both per row).
+constexpr int kMaxCandidates = 8;
+struct MassArgs {
+  float* partial;
+  float* lse_last;
+  int ncand;
+  uint16_t w[kMaxCandidates][3];  // clamped to the grid
+};
+hipError_t launch_mass_bf16(const uint16_t* q, const uint16_t* k, float* lse, const MassArgs& ma,
+                            const Geometry& g, const HeadTable& ht_full, int B, int Hh, int D,
+                            float scale, hipStream_t stream);
+// mass[c][bh] = (sum of partial[c][bh][0 .. S/32)) / real rows.
+hipError_t launch_mass_reduce(const float* partial, float* mass, const Geometry& g, int ncand,
+                              int64_t BH, hipStream_t stream);
 bool bwd_bf16_supported(int D, int L);
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const uint16_t* dout, const float* lse,

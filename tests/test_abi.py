@@ -157,10 +157,11 @@ def test_dense_argument_errors(lib):
 
 
 def test_window_mass_argument_errors(lib):
-    need = lib.sta_window_mass_workspace_bytes(1, 2, d3(6, 16, 16), d3(2, 4, 4))
-    assert need == 2 * 1 * 2 * 1536 * 4                      # two fp32 LSE vectors
-    assert lib.sta_window_mass_workspace_bytes(1, 2, d3(5, 15, 16), d3(2, 4, 4)) == need   # padded
-    assert lib.sta_window_mass_workspace_bytes(0, 2, d3(6, 16, 16), d3(2, 4, 4)) == 0
+    need = lib.sta_window_mass_workspace_bytes(1, 2, d3(6, 16, 16), d3(2, 4, 4), 2)
+    assert need == 2 * 1 * 2 * 1536 * 4 + 2 * 1 * 2 * 48 * 4    # two fp32 LSE vectors + partials
+    assert lib.sta_window_mass_workspace_bytes(1, 2, d3(5, 15, 16), d3(2, 4, 4), 2) == need   # padded
+    assert lib.sta_window_mass_workspace_bytes(0, 2, d3(6, 16, 16), d3(2, 4, 4), 2) == 0
+    assert lib.sta_window_mass_workspace_bytes(1, 2, d3(6, 16, 16), d3(2, 4, 4), 0) == 0
     good = win([(3, 3, 3), (1, 1, 1)])
     bad = win([(3, 3, 3), (1, 0, 1)])
 
@@ -180,6 +181,8 @@ def test_window_mass_argument_errors(lib):
     assert wm(q=MIS) == ALIGN
     assert wm(cands=bad) == WINDOW          # every candidate is checked before the first launch
     assert wm(Hh=257) == UNSUP
+    nine = win([(1, 1, 1)] * 9)
+    assert wm(cands=nine, n=9, nbytes=1 << 30) == UNSUP     # more than STA_MAX_CANDIDATES
 
 
 def test_calib_argument_errors(lib):

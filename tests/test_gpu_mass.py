@@ -64,10 +64,11 @@ def test_window_mass_hunyuan_shape_sampled_and_closed_forms(sta):
     S = int(np.prod(latent))
     x = I.make_inputs(1, Hh, S, D, "bf16", seed=12)
     q, k = (sta.tile_reorder(x[n].to("cuda"), latent, tile) for n in ("q", "k"))
-    ws = torch.empty(sta.window_mass_workspace_bytes(1, Hh, latent, tile), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(sta.window_mass_workspace_bytes(1, Hh, latent, tile, len(cands)), dtype=torch.uint8,
+                     device="cuda")
     mass = to64(sta.window_mass(q, k, latent, tile, cands, workspace=ws))[:, 0, :]
     torch.cuda.synchronize()
-    lse = ws.view(torch.float32).view(2, 1, Hh, S)
+    lse = ws.view(torch.float32)[:2 * Hh * S].view(2, 1, Hh, S)
     lse_full, lse_last = to64(lse[0]), to64(lse[1])
     assert np.abs(mass[0] - 1.0).max() < 1e-6
     assert np.all(mass[5] < mass[1]) and np.all(mass[1] < mass[2]) and np.all(mass[1] < mass[3])
