@@ -83,6 +83,9 @@ class Timer:
     def total_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs)
 
+    def each_ms(self):
+        return sorted(a.elapsed_time(b) for a, b in self.pairs)
+
 
 def source_hash(paths=None):
     """Hash of the forward kernel's code: its source and the headers it uses,
@@ -139,7 +142,18 @@ def cpu_baseline(x, latent, tile, window, head_dim, target_s):
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} query tiles ({done * L} rows) of head 0 of 24, all {L * n[0] * n[1] * n[2]} keys "
                       f"masked, fp64 numpy; {el:.1f} s; value counts the same 4*L^2*D per computed tile "
-                      f"pair as the GPU figure"}
+                      f"pair as the GPU figure; host CPU: {cpu_model()}"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -202,6 +216,7 @@ def main():
     fwd_ms = fwd_timer.total_ms() / args.steps
     log(f"[bench] step {ms_step:.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms), forward kernel {fwd_ms:.3f} ms")
     achieved = flops / (fwd_ms * 1e-3) / 1e12
+    each = fwd_timer.each_ms()   # per-step times of the same timed steps
     traffic = read_traffic()
     result = {
         "metric": "effective TFLOP/s and % bf16 MFMA peak, STA fwd at (30,48,80) latent",
@@ -220,7 +235,8 @@ def main():
                    "head_dim": D, "batch": B, "window": list(wins[0]),
                    "step": "sta_forward_raster: tile reorder of q,k,v and unreorder of o inside the "
                            "forward kernel's loads and stores (one launch)",
-                   "pct_of_peak_step": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+                   "pct_of_peak_step": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                   "step_ms_median": round(each[len(each) // 2], 4), "step_ms_min": round(each[0], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "sta_forward_raster (fwd_bf16_kernel, raster instance)",

@@ -417,13 +417,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 
   // Padded latents: padding rows of a partial query tile are no query; their
   // P (and dS) is zero.  A second walk over the query blocks, for the stage
-  // being computed; returns the real-row bits (all set when nothing is masked).
+  // being computed; returns the stage's 32-row real mask (the same in every
+  // lane; all set when nothing is masked).
   int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
-  auto query_bits = [&]() -> uint32_t {
-    uint32_t bits = 0xffffffffu;
-    if (!g.padded) return bits;
+  auto query_mask = [&]() -> uint32_t {
+    uint32_t m = 0xffffffffu;
+    if (!g.padded) return m;
     const int q0 = lo0 + ci0, q1 = lo1 + ci1, q2 = lo2 + ci2;
-    if (tile_partial(q0, q1, q2, g)) bits = lane_bits(block_real_mask(q0, q1, q2, cjb * kStage, g, lane), lane);
+    if (tile_partial(q0, q1, q2, g)) m = block_real_mask(q0, q1, q2, cjb * kStage, g, lane);
     if (++cjb == spt) {
       cjb = 0;
       if (++ci2 == c2) {
@@ -434,11 +435,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
         }
       }
     }
-    return bits;
+    return m;
   };
 
   auto step = [&](const char* ql, const char* dol, const char* st) {
-    const uint32_t qbits = query_bits();
+    const uint32_t qmask = query_mask();
     f32x16 s, dp;
     {
       bf16x8 qa[KS];
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
       dp = contract_rows<D>(da, vf);  // dP[q][key]
     }
     // lane's queries: 8i + 4g + jj; the A operand is P^T (MODE 0) or dS^T.
-    bf16x8 af[2];
+    float pe[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *(const f32x4*)(st + (8 * i + 4 * grp) * 4);
@@ -461,10 +462,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int e = 4 * i + jj;
-        const float p = elem_real(qbits, e) ? __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj])) : 0.0f;
-        af[e >> 3][e & 7] = MODE == 0 ? (__bf16)p : (__bf16)(p * (dp[e] - d4[jj]));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj]));
+        pe[e] = MODE == 0 ? p : p * (dp[e] - d4[jj]);
       }
     }
+    if (qmask != 0xffffffffu) {  // a stage with padding queries (uniform branch)
+      // kept a branch: if-converted, the selects would run on every stage
+      asm volatile("" ::: "memory");
+      const uint32_t bits = lane_bits(qmask, lane);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!elem_real(bits, e)) pe[e] = 0.0f;
+    }
+    bf16x8 af[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) af[e >> 3][e & 7] = (__bf16)pe[e];
     // B operand: dO^T (MODE 0) or Q^T, read transposed from the staged tile
     // (for dK, not hoisted above the vector work: registers are short).
     if constexpr (MODE == 1) __builtin_amdgcn_sched_barrier(0);
@@ -479,20 +491,24 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   // Two-stage LDS ring: the copy of stage j + 1 is issued before stage j is
   // computed.  Wave 0 also copies the stage statistics, so its waits cover one
   // more copy than the other waves'.
+  // The loop body holds both slots and has no exit in between (an exit
+  // there made the compiler copy the accumulators every other stage); an
+  // odd last stage runs after it.
   issue(ql0, dol0, st0);
   wait_dma();
   barrier_lds();
-  for (int j = 0; j < nst; j += 2) {
-    if (j + 1 < nst) issue(ql1, dol1, st1);
+  int j = 0;
+  for (; j + 1 < nst; j += 2) {
+    issue(ql1, dol1, st1);
     step(ql0, dol0, st0);
     wait_dma();
     barrier_lds();
-    if (j + 1 >= nst) break;
     if (j + 2 < nst) issue(ql0, dol0, st0);
     step(ql1, dol1, st1);
     wait_dma();
     barrier_lds();
   }
+  if (j < nst) step(ql0, dol0, st0);
 
   // dK = scale * acc or dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32;
   // zero on padding rows.
