@@ -292,19 +292,23 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   if (nst > 1) issue(kl1, vl1);
   wait_stage<PER>(nst > 1 ? 1 : 0);   // the dO tile and stage 0 have landed
   barrier_lds();
-  auto stage = [&](int j, const char* kl, const char* vl, char* kf_, char* vf_) {
-    step(kl, vl);
-    if (j + 1 < nst) {
+  // Both slots in one loop body with no exit in between (an exit there made
+  // the compiler copy the accumulators every other stage); an odd last stage
+  // runs after it.
+  int j = 0;
+  for (; j + 1 < nst; j += 2) {
+    step(kl0, vl0);
+    wait_dma();
+    barrier_lds();
+    if (j + 2 < nst) issue(kl0, vl0);
+    step(kl1, vl1);
+    if (j + 2 < nst) {
       wait_dma();
       barrier_lds();
-      if (j + 2 < nst) issue(kf_, vf_);
+      if (j + 3 < nst) issue(kl1, vl1);
     }
-  };
-  for (int j = 0; j < nst; j += 2) {
-    stage(j, kl0, vl0, kl0, vl0);
-    if (j + 1 >= nst) break;
-    stage(j + 1, kl1, vl1, kl1, vl1);
   }
+  if (j < nst) step(kl0, vl0);
 
   // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj; zero
   // on padding rows.
@@ -445,6 +449,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
       bf16x8 qa[KS];
       read_rows<D>(ql, qa, grp, c32);
       s = contract_rows<D>(qa, kf);   // S[q][key]
+      // all Q-row reads first, then the MFMAs (left to itself the compiler
+      // waits for the reads two at a time)
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
     }
     if constexpr (MODE == 1) {
       bf16x8 da[KS], vf[KS];
@@ -486,6 +494,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(af[ss], bt[dt][ss], acc[dt]);
+    if constexpr (MODE == 0) {  // the same for the dO^T reads of dV (not dK: measured slower)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * DT, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DT, 1);
+    }
   };
 
   // Two-stage LDS ring: the copy of stage j + 1 is issued before stage j is
