@@ -140,8 +140,9 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
  * q, k, v, o: bf16 [B, Hh, T*H*W, D] in raster order (W fastest); lse: fp32
  * [B, Hh, T*H*W] raster or NULL.  Needs a whole-tile latent
  * (STA_ERR_NOT_TILE_MULTIPLE otherwise; use the reorder path for padding),
- * STA_BF16 with D in {64, 128}, L % 32 == 0 and the tile width a multiple of
- * 512 / D (STA_ERR_UNSUPPORTED otherwise).  Other arguments as sta_forward. */
+ * STA_BF16 with D in {64, 128}, L % 32 == 0, the tile width a multiple of
+ * 512 / D and L <= 1024 * 512 / D, i.e. 4096 tokens for D = 128 and 8192 for
+ * D = 64 (STA_ERR_UNSUPPORTED otherwise).  Other arguments as sta_forward. */
 int sta_forward_raster(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
                        const int32_t* win_host, float scale, sta_dtype dt, void* stream);

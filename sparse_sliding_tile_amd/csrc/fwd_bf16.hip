@@ -42,6 +42,8 @@ namespace sta {
 namespace {
 
 constexpr float kRescaleThreshold = 8.0f;
+// Copy segments per tile the raster instance tabulates (L / rows-per-segment).
+constexpr int kMaxRasterSegs = 1024;
 
 template <int D, int QT, int NW>
 struct FwdCfg {
@@ -271,6 +273,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
     return key0;
   };
+  // Raster instance: the intra-tile part of the raster row of each copy
+  // segment's first row (the same for every key tile), tabulated once; a
+  // segment's raster row is then its key tile's origin plus the entry.
+  __shared__ uint32_t seg_intra[RASTER ? kMaxRasterSegs : 1];
+  if constexpr (RASTER) {
+    constexpr int RPS = KvDma<D, KB, NW>::RPS;
+    for (int i = tid; i < g.L / RPS; i += C::THREADS) {
+      const uint32_t r = (uint32_t)(i * RPS);
+      const uint32_t t0 = fdiv(r, g.fhw), rem = r - t0 * (uint32_t)(g.h * g.w);
+      const uint32_t t1 = fdiv(rem, g.fw), t2 = rem - t1 * (uint32_t)g.w;
+      seg_intra[i] = (t0 * (uint32_t)g.H + t1) * (uint32_t)g.W + t2;
+    }
+    __syncthreads();
+  }
   const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
   auto issue = [&](char* kl, char* vl) {
     if constexpr (MASS) {
@@ -278,11 +294,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     } else if constexpr (RASTER) {
       // raster rows of this block's segments (scalar: the same in every lane)
       using Cp = KvDma<D, KB, NW>;
+      const uint32_t org = ((uint32_t)((s0 + i0) * g.t) * (uint32_t)g.H + (uint32_t)((s1 + i1) * g.h)) *
+                               (uint32_t)g.W + (uint32_t)((s2 + i2) * g.w);
       uint32_t rows[Cp::PT];
 #pragma unroll
       for (int e = 0; e < Cp::PT; ++e)
-        rows[e] = raster_row(s0 + i0, s1 + i1, s2 + i2,
-                             (uint32_t)(jb * KB + (copier.wave_u + e * NW) * Cp::RPS), g);
+        rows[e] = org + __builtin_amdgcn_readfirstlane(
+                            seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
       next_key0();
       copier.issue_rows(kb, vb, rows, kl, vl);
     } else {
@@ -545,7 +563,8 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 bool fwd_raster_supported(int D, const Geometry& g) {
   // a copy segment (1 KiB) holds 1024 / (2 D) rows; they must be consecutive
   // raster rows, so the tile width must be a multiple of that count
-  return fwd_bf16_supported(D, g.L) && !g.padded && g.w % (512 / D) == 0;
+  return fwd_bf16_supported(D, g.L) && !g.padded && g.w % (512 / D) == 0 &&
+         g.L / (512 / D) <= kMaxRasterSegs;
 }
 
 hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -112,6 +112,8 @@ def test_forward_raster_argument_errors(lib):
     assert fr(tile=(2, 8, 2), latent=(6, 16, 32)) == UNSUP    # copy segments of 4 rows span x-runs
     assert fr(D=64, tile=(2, 8, 4)) == UNSUP                   # D = 64: 8-row segments, width 4 too narrow
     assert fr(D=96) == UNSUP
+    # the raster instance tabulates at most 1024 copy segments per tile: L <= 4096 for D = 128
+    assert fr(latent=(8, 64, 64), tile=(8, 32, 32)) == UNSUP
     assert fr(q=MIS) == ALIGN
     assert fr(lse=MIS) == ALIGN
 
