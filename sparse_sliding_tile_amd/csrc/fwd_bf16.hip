@@ -180,7 +180,7 @@ __device__ __forceinline__ uint32_t raster_row(int a0, int a1, int a2, uint32_t 
 // RASTER: q, k, v, o and lse are in raster order (a latent of whole tiles
 // whose tile width is a multiple of a copy segment's rows): the reorder and
 // unreorder happen in the kernel's own loads and stores.
-template <int D, int QT, int NW, int OCC, bool MASS, bool RASTER>
+template <int D, int QT, int NW, int OCC, bool MASS, bool RASTER, int PADM>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, Geometry g,
@@ -315,9 +315,33 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
   bool tile_done = false;
   uint32_t member = 0;
+  // Padding masks (PADM, one instance each): 0 whole-tile latent, no mask;
+  // 1 tiles 8 keys wide with at most 64 tile rows; 2 any other tile.
+  // PADM 1: a 32-key block is 4 tile rows of 8, and element e of lane l in
+  // the S^T accumulator holds row e / 4 of the block and column 4 (l / 32) +
+  // e % 4 of the tile.  A key is real when its row (i0, i1) and its column
+  // are: one bit per tile row (a ballot) and the tile's real width are worked
+  // out once per key tile, and a stage adds 0 or -inf to the scores of padding
+  // rows and columns (scores are finite, so the sum is exactly -inf).
+  // PADM 2 tests every key of the block (ballot per stage).
+  constexpr bool row_col_mask = PADM == 1;
+  bool key_tile_partial = false, col_partial = false;
+  uint64_t rows_real = ~0ull;  // bit R: tile row R is real
+  int col_ext = 8;             // real columns of the key tile
   auto mask_keys = [&](f32x16 (&sacc)[QT]) {
-    if (!MASS && !g.padded) return;
+    if (!MASS && PADM == 0) return;
     const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
+    if (row_col_mask && cjb == 0) {  // a new key tile
+      key_tile_partial = tile_partial(k0, k1, k2, g);
+      if (key_tile_partial) {
+        const int e0 = tile_ext(k0, g.t, g.T), e1 = tile_ext(k1, g.h, g.H), e2 = tile_ext(k2, g.w, g.W);
+        const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
+        const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
+        rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
+        col_ext = e2;
+        col_partial = e2 < 8;
+      }
+    }
     if constexpr (MASS) {
       tile_done = cjb == bpt - 1;
       member = 0;
@@ -332,7 +356,30 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         }
       }
     }
-    if (g.padded && tile_partial(k0, k1, k2, g)) {
+    if constexpr (row_col_mask) {
+      if (key_tile_partial) {
+        const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
+        if (rb != 0xfu) {  // a row of the block is padding (uniform)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float rbias = (rb >> u) & 1u ? 0.f : -INFINITY;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) sacc[qt][4 * u + jj] += rbias;
+          }
+        }
+        if (col_partial) {  // scores are finite, so adding -inf masks exactly
+          float cb[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) cb[jj] = 4 * grp + jj < col_ext ? 0.f : -INFINITY;
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[qt][e] += cb[e & 3];
+        }
+      }
+    } else if (PADM == 2 && tile_partial(k0, k1, k2, g)) {
       const uint32_t m = block_real_mask(k0, k1, k2, cjb * KB, g, lane);
       if (m != 0xffffffffu) {  // blocks of a partial tile are often whole
         const uint32_t bits = lane_bits(m, lane);
@@ -470,7 +517,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   for (int qt = 0; qt < QT; ++qt) {
     const float lt = xsum32(lrun[qt]);
     const int rin = qrow0 - qtile * g.L + qt * 32 + c32;  // row inside the query tile
-    const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
+    const bool real = PADM == 0 || token_real(a0, a1, a2, rin, g);
     const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow[qt];
     if constexpr (!MASS) {
@@ -522,7 +569,22 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
   const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER>), dim3((uint32_t)total),
+  // Padded latents get instances of their own (the key mask and the zeroed
+  // padding rows); the raster instance takes whole-tile latents only.
+  if constexpr (!RASTER) {
+    if (g.padded) {
+      if (g.w == 8 && g.t * g.h <= 64)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 1>), dim3((uint32_t)total),
+                           dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh,
+                           scale * kLog2e, bpt, total, group);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 2>), dim3((uint32_t)total),
+                           dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh,
+                           scale * kLog2e, bpt, total, group);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 0>), dim3((uint32_t)total),
                      dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh, scale * kLog2e,
                      bpt, total, group);
   return hipGetLastError();

@@ -34,6 +34,7 @@ CASES = [
     ((6, 16, 16), (2, 4, 4), 1, 3, 64, "bf16", [(3, 3, 3), (2, 1, 4), (3, 4, 4)]),
     ((5, 13, 14), (2, 4, 4), 1, 2, 128, "bf16", [(1, 1, 1), (2, 2, 2), (3, 4, 4)]),   # padded to (6, 16, 16)
     ((5, 13, 14), (2, 4, 4), 1, 2, 64, "f32", [(1, 2, 1), (3, 4, 4)]),                # padded, fp32
+    ((3, 12, 13), (2, 8, 8), 1, 2, 128, "bf16", [(1, 1, 1), (2, 2, 2), (1, 2, 2)]),   # padded, 8-wide tiles
     ((1, 40, 48), (1, 8, 8), 1, 2, 128, "bf16", [(1, 3, 3), (1, 5, 5), (1, 1, 1)]),   # 2D, 64-token tiles
 ]
 
