@@ -161,7 +161,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this build has no multi-GPU path; sharding by head is described in DESIGN.md.",
+              "the library has no multi-GPU path (heads are independent, so more GPUs would each take "
+              "a share of the heads).",
               file=sys.stderr)
         sys.exit(2)
 

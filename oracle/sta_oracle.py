@@ -21,7 +21,7 @@ Sources (web pages, cited by title and section):
 What the oracle computes is the plain definition the method reaches exactly:
 full softmax attention whose mask admits key token j for query token i iff the
 tile holding j lies in the window of the tile holding i.  Readings taken where
-the pages are silent (each is listed in the design doc as well):
+the pages are silent:
   * raster order of the latent is (T, H, W) with W fastest;
   * tile-major order: tiles in raster order over the tile grid, tokens in raster
     order inside a tile;
