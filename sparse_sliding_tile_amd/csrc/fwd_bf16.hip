@@ -67,6 +67,23 @@ __device__ __forceinline__ void qk_stage(const bf16x8 (&kf)[D / 16], const bf16x
     for (int qt = 0; qt < QT; ++qt) sacc[qt] = mfma32(kf[ks], qf[qt][ks], sacc[qt]);
 }
 
+// Maximum of a block's 16 scores as a balanced tree (depth 4).  The IEEE
+// maximum (NaN-propagating) needs no operand canonicalisation, which fmaxf
+// (maxNum) inserts for every operand coming straight from an MFMA; the
+// scores are finite, so both give the same value.
+__device__ __forceinline__ float vmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax2(vmax2(a, b), c); }
+__device__ __forceinline__ float block_max16(const f32x16& s) {
+  const float m0 = vmax3(s[0], s[1], s[2]), m1 = vmax3(s[3], s[4], s[5]), m2 = vmax3(s[6], s[7], s[8]);
+  const float m3 = vmax3(s[9], s[10], s[11]), m4 = vmax3(s[12], s[13], s[14]);
+  return vmax2(vmax3(m0, m1, m2), vmax3(m3, m4, s[15]));
+}
+// The same across the two lanes l and l ^ 32 that hold one query's scores.
+__device__ __forceinline__ float xmax32_raw(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax2(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
 // Online softmax of one stage (lazy rescale), producing the bf16 P^T operand.
 template <int D, int QT>
 __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (&pf)[QT][2],
@@ -76,10 +93,7 @@ __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (
   float mblk[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float mx = sacc[qt][0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[qt][e]);
-    mblk[qt] = xmax32(mx) * c_log2;
+    mblk[qt] = xmax32_raw(block_max16(sacc[qt])) * c_log2;
     need |= mblk[qt] > mrun[qt] + kRescaleThreshold;
   }
   if (__any(need)) {
@@ -126,10 +140,7 @@ __device__ __forceinline__ void mass_stage(const f32x16 (&sacc)[QT], float (&mru
                                            bool tile_done, uint32_t member, float c_log2) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float mx = sacc[qt][0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[qt][e]);
-    const float mblk = xmax32(mx) * c_log2;
+    const float mblk = xmax32_raw(block_max16(sacc[qt])) * c_log2;
     if (mblk > mrun[qt] + kRescaleThreshold) {
       const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mblk);
       lfull[qt] *= alpha;
