@@ -139,7 +139,10 @@ def cpu_baseline(x, latent, tile, window, head_dim, target_s):
         if el >= target_s or done >= n[0] * n[1] * n[2]:
             break
     flops = done * kh(window, n) * 4 * L * L * head_dim
+    nt, heads = n[0] * n[1] * n[2], x["q"].shape[1]
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "s_per_query_tile": round(el / done, 4),
+            "extrapolated_s_per_launch": round(el / done * nt * heads, 1),  # x tiles x heads, extrapolated
             "sample": f"{done} query tiles ({done * L} rows) of head 0 of 24, all {L * n[0] * n[1] * n[2]} keys "
                       f"masked, fp64 numpy; {el:.1f} s; value counts the same 4*L^2*D per computed tile "
                       f"pair as the GPU figure; host CPU: {cpu_model()}"}
