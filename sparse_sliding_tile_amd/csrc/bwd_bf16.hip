@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
   if (row < rows && c == 0) {
-    dl[row] = s;
+    dl[row] = -s;  // -Dl: the dK pass starts its dP accumulation from it
     lse2[row] = lse[row] * kLog2e;
   }
 }
@@ -150,6 +150,14 @@ __device__ __forceinline__ f32x16 contract_rows(const bf16x8 (&a)[D / 16], const
   for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(a[ks], b[ks], acc);
   return acc;
 }
+// The same contraction added to acc.
+template <int D>
+__device__ __forceinline__ f32x16 contract_rows_from(const bf16x8 (&a)[D / 16], const bf16x8 (&b)[D / 16],
+                                                     f32x16 acc) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(a[ks], b[ks], acc);
+  return acc;
+}
 
 // --------------------------------------------------------------------------
 // 2. dQ (query-major).  Workgroup = NW waves x 32 query rows of one tile.
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
       dma16(dout + (row0 + r) * D + ((p ^ (int)swz<D>(r)) * 8), dotile + seg * 1024);
     }
   }
-  const float lrow = lse2[row], drow = dl[row];
+  const float lrow = lse2[row], ndrow = dl[row];  // -Dl
 
   const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
   const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * s + e], c_log2, -lrow));
-        ds[s][e] = (__bf16)(p * (dpt[8 * s + e] - drow));
+        ds[s][e] = (__bf16)(p * (dpt[8 * s + e] + ndrow));
       }
     bf16x8 ktf[DT][2];
     read_cols<D>(kl, ktf, lane);
@@ -458,20 +466,27 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
       bf16x8 da[KS], vf[KS];
       read_rows<D>(dol, da, grp, c32);
       read_rows<D>(vtile, vf, grp, c32);
-      dp = contract_rows<D>(da, vf);  // dP[q][key]
+      // dP - Dl: the accumulation starts from -Dl of the element's query
+      // (stage statistics, already in the accumulator's layout)
+      f32x16 ndl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 d4 = *(const f32x4*)(st + 128 + (8 * i + 4 * grp) * 4);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) ndl[4 * i + jj] = d4[jj];
+      }
+      dp = contract_rows_from<D>(da, vf, ndl);  // dP[q][key] - Dl[q]
     }
     // lane's queries: 8i + 4g + jj; the A operand is P^T (MODE 0) or dS^T.
     float pe[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *(const f32x4*)(st + (8 * i + 4 * grp) * 4);
-      f32x4 d4 = {};
-      if constexpr (MODE == 1) d4 = *(const f32x4*)(st + 128 + (8 * i + 4 * grp) * 4);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int e = 4 * i + jj;
         const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c_log2, -l4[jj]));
-        pe[e] = MODE == 0 ? p : p * (dp[e] - d4[jj]);
+        pe[e] = MODE == 0 ? p : p * dp[e];
       }
     }
     if (qmask != 0xffffffffu) {  // a stage with padding queries (uniform branch)
