@@ -150,10 +150,14 @@ __device__ __forceinline__ void mass_stage(const f32x16 (&sacc)[QT], float (&mru
       mrun[qt] = mblk;
     }
     const float mneg = -mrun[qt];
-    float ls = 0.f;
+    float pe[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ls += __builtin_amdgcn_exp2f(fmaf(sacc[qt][e], c_log2, mneg));
-    ltile[qt] += ls;
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][e], c_log2, mneg));
+#pragma unroll
+    for (int w = 8; w > 0; w >>= 1)  // pairwise tree: depth 4 instead of a 16-add chain
+#pragma unroll
+      for (int e = 0; e < w; ++e) pe[e] += pe[e + w];
+    ltile[qt] += pe[0];
     if (tile_done) {
       lfull[qt] += ltile[qt];
 #pragma unroll
