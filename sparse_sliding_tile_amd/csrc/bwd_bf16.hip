@@ -580,7 +580,10 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   // dQ fits two waves per SIMD in 4-wave workgroups; smaller ones keep one.
   hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NW >= 4 ? 2 : 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
                      dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, 2>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
+  // dV asks for two waves per SIMD, except one-wave workgroups at D = 128,
+  // whose registers allow one.
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, (NW >= 2 || D <= 64) ? 2 : 1>), dim3((uint32_t)total),
+                     dim3(64 * NW), 0, st, q,
                      k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
   // dK fits two waves per SIMD in 4-wave workgroups; smaller ones keep one.
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, NW >= 4 ? 2 : 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
