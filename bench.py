@@ -12,9 +12,12 @@ value = counted forward FLOPs per step / step time, where counted FLOPs are
 skipped pair, no softmax).  The JSON line also carries:
   roofline      the sta_forward kernel alone, timed with events on its stream;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the workload;
-  legs          the dense attention kernel of the same build (speedup
-                denominator), the backward at the fine-tuning shape, the mixed
-                per-head window and Wan-shaped forwards, and reorder bandwidth.
+  legs          the same step with separate reorder kernels; dense attention
+                from the same library (speedup denominator); reorder bandwidth;
+                the mixed-window, Wan-shaped, 2D and padded forwards; the
+                backward at the fine-tuning shape, with mixed windows at
+                (30,48,80) and on the padded latent; the window mass of five
+                candidate windows; and a matrix-core calibration loop.
 Everything runs on one GPU; --gpus above 1 is refused.
 """
 import argparse
@@ -325,9 +328,10 @@ def main():
             if lname.endswith("mixed"):
                 legs[lname]["windows"] = [list(x_) for x_ in lw["windows"]]
             del a, b_, c, out, ll
-        # backward at the fine-tuning shape, and at the HunyuanVideo shape with
-        # the mixed per-head windows
-        for bname, iters in (("finetune_24x64x64_w355", 3), ("hunyuan_30x48x80_mixed", 2)):
+        # backward at the fine-tuning shape, at the HunyuanVideo shape with the
+        # mixed per-head windows, and on the padded latent (29,45,76)
+        for bname, iters in (("finetune_24x64x64_w355", 3), ("hunyuan_30x48x80_mixed", 2),
+                             ("hunyuan_29x45x76_w333_padded", 2)):
             fw = I.WORKLOADS[bname]
             fS = sta.tile_major_len(fw["latent"], fw["tile"])
             shape = (fw["batch"], fw["heads"], fS, fw["head_dim"])
@@ -346,7 +350,7 @@ def main():
             legs[bname + "_backward"] = {
                 "ms": round(bms, 3), "tflops": round(bflops / bms / 1e9, 1),
                 "pct_of_peak": round(100 * bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                "counted": "10*L^2*D per tile pair (5 GEMMs); the kernels run 8 (dQ, dV and dK passes)"}
+                "counted": "10*L^2*D per tile pair (5 GEMMs, padded grid for a padded latent); the kernels run 8 (dQ, dV and dK passes)"}
             del a, b_, c, do, out, ll, ws
         # window search, measurement side: attention mass of the five
         # candidate windows of the mixed-window workload, all 24 heads
