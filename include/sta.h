@@ -148,7 +148,8 @@ int sta_forward_raster(const void* q, const void* k, const void* v, void* o, flo
                        const int32_t* win_host, float scale, sta_dtype dt, void* stream);
 
 /* Bytes of device workspace sta_backward needs: 8*B*Hh*S' for per-row
- * statistics (fp32: Dl, held negated by the bf16 path, and LSE*log2(e)) plus,
+ * statistics (fp32: Dl, held negated by the bf16 path, and LSE*log2(e); on
+ * padding rows 0 and +inf) plus,
  * for STA_BF16, 4*Hh*n0*n1*n2 for a per-head order of the key tiles.  0 for
  * invalid sizes. */
 size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 latent,

@@ -21,6 +21,8 @@
 // The operand layouts, LDS swizzle and transposed reads are those of
 // mfma_common.h; a transposed read of a row-major [32 x D] tile gives the
 // operand [d][row] with the row order of the accumulator (see fwd_bf16.hip).
+#include <type_traits>
+
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -32,14 +34,18 @@ constexpr int kStage = 32;  // rows (keys or queries) per pipeline stage
 
 // --------------------------------------------------------------------------
 // 1. prep: Dl_i = <dO_i, O_i> (fp32) and lse2_i = LSE_i * log2(e).
-//    D/8 lanes per row, 16-byte loads, shuffle reduction.
+//    D/8 lanes per row, 16-byte loads, shuffle reduction.  Padding rows of a
+//    padded latent get lse2 = +inf and Dl = 0: with finite scores every P of
+//    such a query is then exactly zero, so the dK/dV passes need no query mask
+//    and dQ is zero there by construction.
 // --------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ lse2,
-                                                       float* __restrict__ dl, size_t rows) {
+                                                       float* __restrict__ dl, size_t rows,
+                                                       Geometry g) {
   constexpr int LPR = D / 8;  // lanes per row
   const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int c = threadIdx.x % LPR;
@@ -56,8 +62,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
   if (row < rows && c == 0) {
-    dl[row] = -s;  // -Dl: the dK pass starts its dP accumulation from it
-    lse2[row] = lse[row] * kLog2e;
+    bool real = true;
+    if (g.padded) {
+      const int r = (int)(row % (size_t)g.S), tile = r / g.L;
+      const int a2 = tile % g.n2, a1 = (tile / g.n2) % g.n1, a0 = tile / (g.n2 * g.n1);
+      real = token_real(a0, a1, a2, r - tile * g.L, g);
+    }
+    dl[row] = real ? -s : 0.f;  // -Dl: the dK pass starts its dP accumulation from it
+    lse2[row] = real ? lse[row] * kLog2e : INFINITY;
   }
 }
 
@@ -162,7 +174,9 @@ __device__ __forceinline__ f32x16 contract_rows_from(const bf16x8 (&a)[D / 16], 
 // --------------------------------------------------------------------------
 // 2. dQ (query-major).  Workgroup = NW waves x 32 query rows of one tile.
 // --------------------------------------------------------------------------
-template <int D, int NW, int OCC>
+// PADM: 0 no padding; 1 padded latent with w = 8 and t*h <= 64 (row and column
+// mask); 2 any other padded latent (a ballot per partial stage).
+template <int D, int NW, int OCC, int PADM>
 __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
@@ -239,11 +253,49 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
 
   // Padded latents: keys at padding positions of a partial key tile get
   // P = 0 (a second walk over the key blocks, for the stage being computed).
+  // The S^T accumulator holds key 8i + 4(l/32) + jj of the stage in element
+  // 4i + jj: with w = 8 that is row 4 cjb + i of the tile and column
+  // 4(l/32) + jj, so one bit per tile row (a ballot) and the tile's real width,
+  // worked out once per key tile, mask a stage by adding 0 or -inf (scores are
+  // finite, so the sum is exactly -inf).  PADM 2 tests every key of the block.
   int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  bool key_tile_partial = false, col_partial = false;
+  uint64_t rows_real = ~0ull;  // bit R: tile row R is real
+  int col_ext = 8;             // real columns of the key tile
   auto mask_keys = [&](f32x16& st) {
-    if (!g.padded) return;
+    if constexpr (PADM == 0) return;
     const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
-    if (tile_partial(k0, k1, k2, g)) {
+    if constexpr (PADM == 1) {
+      if (cjb == 0) {  // a new key tile
+        key_tile_partial = tile_partial(k0, k1, k2, g);
+        if (key_tile_partial) {
+          const int e0 = tile_ext(k0, g.t, g.T), e1 = tile_ext(k1, g.h, g.H), e2 = tile_ext(k2, g.w, g.W);
+          const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
+          const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
+          rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
+          col_ext = e2;
+          col_partial = e2 < 8;
+        }
+      }
+      if (key_tile_partial) {
+        const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
+        if (rb != 0xfu) {  // a row of the block is padding (uniform)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float rbias = (rb >> u) & 1u ? 0.f : -INFINITY;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) st[4 * u + jj] += rbias;
+          }
+        }
+        if (col_partial) {
+          float cb[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) cb[jj] = 4 * grp + jj < col_ext ? 0.f : -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) st[e] += cb[e & 3];
+        }
+      }
+    } else if (tile_partial(k0, k1, k2, g)) {
       const uint32_t m = block_real_mask(k0, k1, k2, cjb * kStage, g, lane);
       if (m != 0xffffffffu) {
         const uint32_t bits = lane_bits(m, lane);
@@ -270,6 +322,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     read_rows<D>(vl, vr, grp, c32);
     f32x16 st = contract_rows<D>(kf, qf);         // S^T[key][q]
     mask_keys(st);
+    // a scheduling boundary after the mask (the dP^T reads stay below it:
+    // measured faster)
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 dpt;
     {
       bf16x8 dof[KS];
@@ -427,31 +482,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  // Padded latents: padding rows of a partial query tile are no query; their
-  // P (and dS) is zero.  A second walk over the query blocks, for the stage
-  // being computed; returns the stage's 32-row real mask (the same in every
-  // lane; all set when nothing is masked).
-  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
-  auto query_mask = [&]() -> uint32_t {
-    uint32_t m = 0xffffffffu;
-    if (!g.padded) return m;
-    const int q0 = lo0 + ci0, q1 = lo1 + ci1, q2 = lo2 + ci2;
-    if (tile_partial(q0, q1, q2, g)) m = block_real_mask(q0, q1, q2, cjb * kStage, g, lane);
-    if (++cjb == spt) {
-      cjb = 0;
-      if (++ci2 == c2) {
-        ci2 = 0;
-        if (++ci1 == c1) {
-          ci1 = 0;
-          ++ci0;
-        }
-      }
-    }
-    return m;
-  };
-
+  // Padding queries of a padded latent need no mask here: their lse2 is +inf,
+  // so their P (and dS) is exactly zero.
   auto step = [&](const char* ql, const char* dol, const char* st) {
-    const uint32_t qmask = query_mask();
     f32x16 s, dp;
     {
       bf16x8 qa[KS];
@@ -489,14 +522,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
         pe[e] = MODE == 0 ? p : p * dp[e];
       }
     }
-    if (qmask != 0xffffffffu) {  // a stage with padding queries (uniform branch)
-      // kept a branch: if-converted, the selects would run on every stage
-      asm volatile("" ::: "memory");
-      const uint32_t bits = lane_bits(qmask, lane);
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (!elem_real(bits, e)) pe[e] = 0.0f;
-    }
+    // the second GEMM's operand reads start after the exponentials (measured
+    // faster for dV than the compiler's interleave; dK is indifferent)
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 af[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) af[e >> 3][e & 7] = (__bf16)pe[e];
@@ -572,14 +600,21 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   hipLaunchKernelGGL(bwd_rank_kernel, dim3((uint32_t)Hh), dim3(256), 0, st, g, ht, rank_tab);
   const size_t threads = rows * (D / 8);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
-                     st, o, dout, lse, lse2, dl, rows);
+                     st, o, dout, lse, lse2, dl, rows, g);
   const int bpt = g.L / (NW * 32);
   const int total = B * Hh * g.ntiles * bpt;
   const int group = group_items_for(B * Hh, g.ntiles * bpt);
   const float c_log2 = scale * kLog2e;
   // dQ fits two waves per SIMD in 4-wave workgroups; smaller ones keep one.
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NW >= 4 ? 2 : 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v,
-                     dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+  // The padding mode is a template argument: mask code costs registers.
+  auto dq_pass = [&](auto padm) {
+    constexpr int PADM = decltype(padm)::value;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NW >= 4 ? 2 : 1, PADM>), dim3((uint32_t)total), dim3(64 * NW), 0,
+                       st, q, k, v, dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
+  };
+  if (!g.padded) dq_pass(std::integral_constant<int, 0>{});
+  else if (g.w == 8 && g.t * g.h <= 64) dq_pass(std::integral_constant<int, 1>{});
+  else dq_pass(std::integral_constant<int, 2>{});
   // dV asks for two waves per SIMD, except one-wave workgroups at D = 128,
   // whose registers allow one.
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, (NW >= 2 || D <= 64) ? 2 : 1>), dim3((uint32_t)total),
