@@ -52,6 +52,37 @@ def test_backward_bf16_small(sta, latent, tile, B, wins, D):
         assert e["max_abs"] < BF16_TOL and e["rel_rms"] < BF16_REL_RMS, name
 
 
+@pytest.mark.parametrize("latent,tile", [((11, 30, 29), (2, 8, 8)), ((5, 15, 13), (2, 4, 4))])
+def test_backward_bf16_padding_contents(sta, latent, tile):
+    """Padding rows of q, k, v and dout filled with large finite values (the
+    header asks only for finite contents there): the gradients of real rows
+    match the oracle on zero-padded inputs and padding rows stay zero.  Covers
+    both key-mask modes of the dQ pass (tile width 8 and 4) and the dK/dV
+    pass, which relies on the +inf statistics of padding queries."""
+    wins = [(3, 3, 3), (2, 1, 3)]
+    S = int(np.prod(latent))
+    x = I.make_inputs(1, len(wins), S, 128, "bf16", seed=21, with_do=True)
+    scale = 128 ** -0.5
+    pad = torch.from_numpy(~O.valid_positions(latent, tile)).to("cuda")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    t = {}
+    for n in ("q", "k", "v", "do"):
+        y = _tm(sta, x[n], latent, tile).clone()
+        junk = (torch.rand(y.shape, generator=g) * 60 - 30).to(torch.bfloat16).to("cuda")
+        y[:, :, pad] = junk[:, :, pad]
+        t[n] = y
+    o, lse = sta.forward(t["q"], t["k"], t["v"], latent, tile, wins, scale=scale)
+    dq, dk, dv = sta.backward(t["q"], t["k"], t["v"], o, t["do"], lse, latent, tile, wins, scale=scale)
+    ref = O.backward(*(O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v", "do")),
+                     latent, tile, wins, scale)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        assert bool(torch.isfinite(got.float()).all()), name
+        assert float(got[:, :, pad].float().abs().max()) == 0.0, name
+        e = err_report(to64(got), r)
+        print(name, e)
+        assert e["max_abs"] < BF16_TOL and e["rel_rms"] < BF16_REL_RMS, name
+
+
 def test_backward_bf16_zero_query(sta):
     """Q = 0: P is uniform over each window, so dV_j is the mean-weighted sum of
     dO over the queries that see key j; pins the transposed window walk."""
