@@ -247,11 +247,10 @@ def window_mask(latent, tile, win, order="tile", rows=None, cols=None):
     kc = tc if cols is None else tc[np.asarray(cols)]
     m = np.ones((qc.shape[0], kc.shape[0]), dtype=bool)
     for d in range(3):
-        wp = min(int(win[d]), n[d])
-        if int(win[d]) < 1:
-            raise ValueError("window must be at least one tile")
-        start = np.clip(qc[:, d] - wp // 2, 0, n[d] - wp)
-        m &= (kc[None, :, d] >= start[:, None]) & (kc[None, :, d] < start[:, None] + wp)
+        # the window of every query tile coordinate along d, from window_start
+        table = np.array([window_start(c, win[d], n[d]) for c in range(n[d])], dtype=np.int64)
+        start, width = table[qc[:, d], 0], table[qc[:, d], 1]
+        m &= (kc[None, :, d] >= start[:, None]) & (kc[None, :, d] < (start + width)[:, None])
     return m
 
 

@@ -399,37 +399,67 @@ def test_backward_query_rows_matches_full():
 
 
 # ---------------------------------------------------------------- planted mistakes
+#
+# Every window decision of the oracle (pairs, masks, forward, backward, mass)
+# goes through window_start.  A mistake planted there must make the pins above
+# fail: the worked start sequences and the scalar brute-force forward, which
+# builds its windows with its own sliding rule and so does not see the plant.
 
-def test_pins_catch_planted_window_mistake(monkeypatch):
-    """A window start one tile too low must fail the worked-sequence pin and
-    the brute-force forward pin."""
-    real = O.window_start
+WORKED_STARTS = [(4, 3, [0, 0, 1, 1]), (6, 3, [0, 0, 1, 2, 3, 3]),
+                 (10, 5, [0, 0, 0, 1, 2, 3, 4, 5, 5, 5])]
 
-    def shifted(q, w, n):
+
+def _pin_worked_sequences():
+    for n, w, starts in WORKED_STARTS:
+        assert [O.sta_oracle.window_start(q, w, n)[0] for q in range(n)] == starts
+
+
+def _pin_forward_brute_force():
+    latent, tile = (4, 8, 12), (2, 4, 4)    # tile grid 2x2x3, 384 tokens
+    wins = [(1, 1, 3), (2, 1, 1)]
+    q, k, v = (_rand((1, 2, 384, 3), s) for s in (70, 71, 72))
+    ref_o, ref_l = _brute_force_raster(q, k, v, latent, tile, wins, 0.6)
+    o, l = O.sta_oracle.forward(q, k, v, latent, tile, wins, 0.6, order="raster")
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, ref_l, rtol=0, atol=1e-12)
+
+
+def test_pins_hold_unplanted():
+    _pin_worked_sequences()
+    _pin_forward_brute_force()
+
+
+@pytest.mark.parametrize("plant", ["shift_low", "shift_high", "truncate"])
+def test_pins_catch_planted_window_mistake(monkeypatch, plant):
+    """Each planted window mistake fails the worked-sequence pin and the
+    brute-force forward pin."""
+    real = O.sta_oracle.window_start
+
+    def planted(q, w, n):
         s, wp = real(q, w, n)
-        return max(s - 1, 0), wp
-    monkeypatch.setattr(O.sta_oracle, "window_start", shifted)
-    assert [O.sta_oracle.window_start(q, 3, 6)[0] for q in range(6)] != [0, 0, 1, 2, 3, 3]
+        if plant == "shift_low":       # window one tile too low (clamped at 0)
+            return max(s - 1, 0), wp
+        if plant == "shift_high":      # window one tile too high (clamped at the edge)
+            return min(s + 1, int(n) - wp), wp
+        # truncate at the grid edge instead of clamping the centre: the
+        # window is cut short where it would leave the grid
+        lo = int(q) - wp // 2
+        hi = lo + wp
+        return max(lo, 0), min(hi, int(n)) - max(lo, 0)
+    monkeypatch.setattr(O.sta_oracle, "window_start", planted)
+    with pytest.raises(AssertionError):
+        _pin_worked_sequences() if plant != "truncate" else _pin_count_invariant()
+    with pytest.raises(AssertionError):
+        _pin_forward_brute_force()
 
 
-def test_pins_catch_planted_mask_mistake(monkeypatch):
-    """A mask that truncates windows at the grid edge (instead of clamping the
-    centre) changes the forward output and fails the count invariant."""
-    def truncated(latent, tile, win, order="tile", rows=None):
-        n, _ = O.tile_grid(latent, tile)
-        kc = O.token_tile_coords(latent, tile, order)
-        qc = kc if rows is None else kc[np.asarray(rows)]
-        m = np.ones((qc.shape[0], kc.shape[0]), dtype=bool)
-        for d in range(3):
-            r = min(win[d], n[d]) // 2
-            m &= np.abs(kc[None, :, d] - qc[:, None, d]) <= r
-        return m
-    latent, tile = (6, 12, 12), (2, 4, 4)    # tile grid 3x3x3
-    q, k, v = (_rand((1, 1, 864, 3), s) for s in (40, 41, 42))
-    good, _ = O.forward(q, k, v, latent, tile, [(3, 3, 3)], 0.5, order="raster")
-    monkeypatch.setattr(O.sta_oracle, "window_mask", truncated)
-    bad, _ = O.sta_oracle.forward(q, k, v, latent, tile, [(3, 3, 3)], 0.5, order="raster")
-    assert np.abs(bad - good).max() > 1e-3
+def _pin_count_invariant():
+    """Every query tile sees prod w' key tiles (the pair-count pin)."""
+    latent, tile, wins = (6, 16, 16), (2, 4, 4), [(3, 3, 3)]
+    n, _ = O.tile_grid(latent, tile)
+    pairs, _ = O.sta_oracle.tile_pairs(latent, tile, wins)
+    counts = np.bincount(pairs[:, 0], minlength=int(np.prod(n)))
+    assert np.all(counts == 27)
 
 
 # ---------------------------------------------------------------- padding with masking
