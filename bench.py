@@ -379,16 +379,17 @@ def main():
         del a, b_, ws, mass
         # the matrix cores alone on N(0, 1) bf16 operands and on zeros: the rate
         # the power limit leaves on data like the inputs, next to the nominal peak
+        from sparse_sliding_tile_amd import calib
         ceil = {}
         for kind in ("randn", "zeros"):
             ops = rand((1 << 19,)) if kind == "randn" else torch.zeros(1 << 19, dtype=torch.bfloat16, device=dev)
-            cout, cfl = sta.calib_mfma_bf16(ops, 20000, 512)
+            cout, cfl = calib.calib_mfma_bf16(ops, 20000, 512)
             for _ in range(60):
-                sta.calib_mfma_bf16(ops, 20000, 512, out=cout)
+                calib.calib_mfma_bf16(ops, 20000, 512, out=cout)
             t = Timer(torch)
             for _ in range(40):
                 with t:
-                    sta.calib_mfma_bf16(ops, 20000, 512, out=cout)
+                    calib.calib_mfma_bf16(ops, 20000, 512, out=cout)
             torch.cuda.synchronize()
             ceil[kind] = cfl / (t.total_ms() / 40) / 1e9
             del ops, cout

@@ -77,7 +77,8 @@ enum {
   STA_ERR_ALIGN = -5,             /* a tensor pointer not 16-byte aligned */
   STA_ERR_HIP = -6,               /* the HIP runtime reported an error at launch */
   STA_ERR_WORKSPACE = -7,         /* workspace missing or smaller than required */
-  STA_ERR_TOO_LARGE = -8          /* a size exceeds the kernels' 32-bit index range */
+  STA_ERR_TOO_LARGE = -8          /* a size exceeds the kernels' index range (32-bit rows,
+                                     at most 65535 tiles along each grid dimension) */
 };
 
 #define STA_MAX_HEADS 256
@@ -126,7 +127,7 @@ int sta_tile_pairs_host(int32_t* pairs_host, int64_t* head_offsets_host, sta_dim
  * q, k, v, o: [B, Hh, S', D] in TILE-MAJOR order (see sta_tile_reorder).
  * lse: fp32 [B, Hh, S'] or NULL.  scale > 0 (usually 1/sqrt(D)).
  * STA_BF16: bf16 in/out, fp32 accumulation, MFMA; needs D in {64, 128} and
- * L % 32 == 0.  STA_F32: fp32 in/out, fp32 arithmetic; needs D <= 128. */
+ * L % 32 == 0.  STA_F32: fp32 in/out, fp32 arithmetic; needs D in {32, 64, 128}. */
 int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                 int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
                 float scale, sta_dtype dt, void* stream);
@@ -206,20 +207,6 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
                     int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
                     const int32_t* cand_host, int64_t n_cand, float scale, sta_dtype dt,
                     void* stream);
-
-/* Measurement support, not part of the method: a bf16 matrix-core loop
- * (v_mfma_f32_32x32x16_bf16, 16 per thread per iteration, four independent
- * accumulator chains, no memory traffic) whose operands are taken from the
- * caller's buffer, so its rate shows what the matrix cores sustain on data
- * drawn like the attention inputs (their power draw, and with it the clock
- * under the board's power limit, depends on the operand values).
- * operands: device, operand_bytes a power of two >= 256 (16-byte aligned);
- * blocks workgroups of 256 threads each run iters iterations: the launch does
- * blocks*256/64 waves * iters * 16 * 32768 FLOP.  out: device fp32
- * [blocks*256], overwritten with per-thread sums (so the work is kept).
- * Asynchronous on stream; time it with events. */
-int sta_calib_mfma_bf16(const void* operands, int64_t operand_bytes, int64_t iters, int64_t blocks,
-                        float* out, void* stream);
 
 #if defined(__GNUC__)
 #pragma GCC visibility pop

@@ -42,7 +42,6 @@ SIGNATURES = {
     "sta_dense_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
                                          c_f32, ctypes.c_int, c_vp]),
     "sta_window_mass_workspace_bytes": (c_sz, [c_i64, c_i64, Dim3, Dim3, c_i64]),
-    "sta_calib_mfma_bf16": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "sta_window_mass": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_sz, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
                                        c_i64, c_f32, ctypes.c_int, c_vp]),
 }
@@ -307,13 +306,3 @@ def window_mass(q, k, latent, tile, candidates, scale=None, workspace=None, out=
                                  _dim3(tile), c.ctypes.data_as(c_vp), c.shape[0], scale, _dtype(q), _stream(q)),
            "sta_window_mass")
     return out
-
-
-def calib_mfma_bf16(operands, iters, blocks, out=None):
-    """Launch the matrix-core calibration loop on ``operands`` (a device bf16
-    tensor of a power-of-two byte size); returns (out, FLOP of the launch)."""
-    nbytes = operands.numel() * operands.element_size()
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=operands.device) if out is None else out
-    _check(lib().sta_calib_mfma_bf16(_dev(operands, "operands"), nbytes, int(iters), int(blocks),
-                                     _dev(out, "out"), _stream(operands)), "sta_calib_mfma_bf16")
-    return out, blocks * 4 * int(iters) * 16 * 32768

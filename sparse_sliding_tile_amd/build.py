@@ -1,4 +1,5 @@
-"""Builds libsta.so in-tree with hipcc for gfx950.
+"""Builds libsta.so (and the benchmark's libsta_calib.so) in-tree with hipcc
+for gfx950.
 
 Usage: python -m sparse_sliding_tile_amd.build  (or call build()).
 """
@@ -10,7 +11,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsta.so")
-SOURCES = ["api.hip", "reorder.hip", "f32_debug.hip", "fwd_bf16.hip", "bwd_bf16.hip", "mass.hip", "calib.hip"]
+SOURCES = ["api.hip", "reorder.hip", "f32_debug.hip", "fwd_bf16.hip", "bwd_bf16.hip", "mass.hip"]
+# the matrix-core calibration loop the benchmark times: its own library, not
+# part of libsta's interface
+CALIB_SOURCES = ["calib.hip"]
+CALIB_LIB = os.path.join(HERE, "libsta_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -22,10 +27,9 @@ FLAGS = [
 ]
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile every HIP source into sparse_sliding_tile_amd/libsta.so."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(sources, out, verbose, extra_flags):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *extra_flags, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -36,8 +40,14 @@ def build(verbose=False, extra_flags=()):
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False, extra_flags=()):
+    """Compile every HIP source: libsta.so and libsta_calib.so, in-tree."""
+    _compile(CALIB_SOURCES, CALIB_LIB, verbose, extra_flags)
+    return _compile(SOURCES, LIB, verbose, extra_flags)
 
 
 if __name__ == "__main__":

@@ -30,6 +30,8 @@ int make_geometry(sta_dim3 latent, sta_dim3 tile, Geometry* g) {
   const int64_t L = (int64_t)tile.t * tile.h * tile.w;
   const int64_t S = n0 * n1 * n2 * L;
   if (L >= (1ll << 31) || S >= (1ll << 31)) return STA_ERR_TOO_LARGE;
+  // Clamped window widths travel to the kernels as 16-bit values.
+  if (n0 > kMaxGridTiles || n1 > kMaxGridTiles || n2 > kMaxGridTiles) return STA_ERR_TOO_LARGE;
   g->T = latent.t;
   g->H = latent.h;
   g->W = latent.w;
@@ -377,17 +379,6 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
     if (e == hipSuccess) e = launch_mass(lse_win, lse_full, mass + c * B * Hh, g, B * Hh, s);
   }
   return to_status(e);
-}
-
-int sta_calib_mfma_bf16(const void* operands, int64_t operand_bytes, int64_t iters, int64_t blocks,
-                        float* out, void* stream) {
-  if (!operands || !out || iters < 1 || blocks < 1) return STA_ERR_ARG;
-  const int64_t vecs = operand_bytes / 16;
-  if (vecs < 16 || (vecs & (vecs - 1)) != 0 || operand_bytes % 16 != 0) return STA_ERR_ARG;
-  if (iters >= (1ll << 31) || blocks >= (1ll << 31) / 256) return STA_ERR_TOO_LARGE;
-  if (misaligned(operands) || misaligned(out)) return STA_ERR_ALIGN;
-  return to_status(
-      launch_calib_mfma(operands, vecs, (int)iters, (int)blocks, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,8 +1,9 @@
 // Matrix-core calibration loop: the bf16 MFMA rate this GPU sustains on
 // operands drawn like the attention inputs, with nothing else running.
 //
-// Not part of the attention method: it gives the measurement a second
-// reference next to the published dense peak.  Operand values decide how much
+// Not part of the attention method and not part of libsta: it is built as
+// its own library, libsta_calib.so, for the benchmark, and gives the
+// measurement a second reference next to the published dense peak.  Operand values decide how much
 // power the matrix cores draw, and under the board's power limit that sets the
 // clock; a loop on all-zero operands runs at the top clock, a loop on N(0, 1)
 // bf16 operands may not.  Each wave keeps eight A and eight B fragments (taken
@@ -49,11 +50,28 @@ __global__ __launch_bounds__(kCalibThreads) void calib_mfma_kernel(const u32x4* 
 
 }  // namespace
 
-hipError_t launch_calib_mfma(const void* src, int64_t src_vectors, int iters, int blocks, float* out,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(calib_mfma_kernel, dim3((uint32_t)blocks), dim3(kCalibThreads), 0, st,
-                     (const u32x4*)src, (uint32_t)(src_vectors - 1), iters, out);
-  return hipGetLastError();
-}
-
 }  // namespace sta
+
+// int sta_calib_mfma_bf16(const void* operands, int64_t operand_bytes,
+//                         int64_t iters, int64_t blocks, float* out, void* stream)
+// operands: device buffer, operand_bytes a power of two >= 256, 16-byte
+// aligned; blocks workgroups of 256 threads each run iters iterations of 16
+// v_mfma_f32_32x32x16_bf16 per wave, i.e. blocks * 4 * iters * 16 * 32768 FLOP
+// per launch.  out: device fp32 [blocks * 256], overwritten with per-thread
+// sums (so the work is kept).  Asynchronous on stream (a hipStream_t, NULL =
+// the null stream); returns 0, -1 for a bad argument, -5 for a misaligned
+// pointer, -6 when the launch fails.
+extern "C" __attribute__((visibility("default"))) int sta_calib_mfma_bf16(
+    const void* operands, int64_t operand_bytes, int64_t iters, int64_t blocks, float* out,
+    void* stream) {
+  if (!operands || !out || iters < 1 || blocks < 1 || iters >= (1ll << 31) ||
+      blocks >= (1ll << 31) / sta::kCalibThreads)
+    return -1;
+  const int64_t vecs = operand_bytes / 16;
+  if (vecs < 16 || (vecs & (vecs - 1)) != 0 || operand_bytes % 16 != 0) return -1;
+  if (((uintptr_t)operands & 15u) || ((uintptr_t)out & 15u)) return -5;
+  hipLaunchKernelGGL(sta::calib_mfma_kernel, dim3((uint32_t)blocks), dim3(sta::kCalibThreads), 0,
+                     (hipStream_t)stream, (const sta::u32x4*)operands, (uint32_t)(vecs - 1),
+                     (int)iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}

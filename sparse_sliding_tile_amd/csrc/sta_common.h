@@ -105,6 +105,10 @@ STA_HD bool token_real(int a0, int a1, int a2, int i, const Geometry& g) {
   return (int)i0 < tile_ext(a0, g.t, g.T) && i1 < tile_ext(a1, g.h, g.H) && i2 < tile_ext(a2, g.w, g.W);
 }
 
+// Largest tile count along one grid dimension: clamped window widths are held
+// in 16 bits (HeadTable, MassArgs).
+constexpr int64_t kMaxGridTiles = 65535;
+
 // Per-head windows, already clamped to the grid (w'), plus a launch order of
 // the heads (heaviest first) for load balance.  Lives in the kernel arguments,
 // so each launch carries its own copy.

@@ -187,15 +187,31 @@ def test_window_mass_argument_errors(lib):
     assert wm(cands=nine, n=9, nbytes=1 << 30) == UNSUP     # more than STA_MAX_CANDIDATES
 
 
-def test_calib_argument_errors(lib):
-    f = lib.sta_calib_mfma_bf16
+def test_calib_library_argument_errors():
+    """The calibration loop lives in its own library (benchmark support, not
+    libsta's interface) and validates before launching."""
+    from sparse_sliding_tile_amd import calib
+    f = calib.lib().sta_calib_mfma_bf16
     assert f(NUL, 1 << 20, 10, 4, P, NUL) == ARG
     assert f(P, 1 << 20, 10, 4, NUL, NUL) == ARG
     assert f(P, 3 << 16, 10, 4, P, NUL) == ARG        # not a power of two
     assert f(P, 128, 10, 4, P, NUL) == ARG            # fewer than 16 vectors
     assert f(P, 1 << 20, 0, 4, P, NUL) == ARG
-    assert f(P, 1 << 20, 10, 1 << 40, P, NUL) == TOO_LARGE
+    assert f(P, 1 << 20, 10, 1 << 40, P, NUL) == ARG
     assert f(MIS, 1 << 20, 10, 4, P, NUL) == ALIGN
+
+
+def test_grid_dimension_limit(lib):
+    """Clamped windows reach the kernels as 16-bit widths: a tile grid with
+    more than 65535 tiles along a dimension is refused, never wrapped."""
+    full = win([(1, 1, 65536)])
+    fp = full.ctypes.data_as(ctypes.c_void_p)
+    assert lib.sta_tile_pairs_count(d3(1, 1, 65535 * 32), d3(1, 1, 32), fp, 1) == 65535 * 65535
+    assert lib.sta_tile_pairs_count(d3(1, 1, 65536 * 32), d3(1, 1, 32), fp, 1) == TOO_LARGE
+    assert lib.sta_tile_pairs_count(d3(65536, 1, 1), d3(1, 1, 1), fp, 1) == TOO_LARGE
+    # dense attention over 2^23 tokens picks 128-token tiles: 65536 of them
+    assert lib.sta_dense_forward(P, P, P, P, NUL, 1, 2, 1 << 23, 128, 0.1, 0, NUL) == TOO_LARGE
+    assert fwd(lib, latent=(1, 1, 65536 * 32), tile=(1, 1, 32), windows=((1, 1, 3), (1, 1, 3))) == TOO_LARGE
 
 
 def test_pairs_argument_errors(lib):

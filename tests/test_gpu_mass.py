@@ -94,15 +94,17 @@ def test_window_mass_hunyuan_shape_sampled_and_closed_forms(sta):
 
 
 def test_calibration_loop_closed_form(sta):
-    """The matrix-core calibration loop on all-ones bf16 operands: each of the
-    four accumulator chains takes 4 MFMAs of 16 ones per iteration, so every
-    thread's sum over its 4 x 16 accumulator elements is 4096 * iters."""
+    """The matrix-core calibration loop (libsta_calib.so, benchmark support) on
+    all-ones bf16 operands: each of the four accumulator chains takes 4 MFMAs
+    of 16 ones per iteration, so every thread's sum over its 4 x 16
+    accumulator elements is 4096 * iters."""
+    from sparse_sliding_tile_amd import calib
     ops = torch.ones(1 << 12, dtype=torch.bfloat16, device="cuda")
-    out, flop = sta.calib_mfma_bf16(ops, 10, 8)
+    out, flop = calib.calib_mfma_bf16(ops, 10, 8)
     torch.cuda.synchronize()
     assert flop == 8 * 4 * 10 * 16 * 32768
     assert torch.equal(out, torch.full_like(out, 4096.0 * 10))
     zeros = torch.zeros(1 << 12, dtype=torch.bfloat16, device="cuda")
-    out0, _ = sta.calib_mfma_bf16(zeros, 10, 8)
+    out0, _ = calib.calib_mfma_bf16(zeros, 10, 8)
     torch.cuda.synchronize()
     assert not out0.any()
