@@ -29,8 +29,10 @@
  *     tiles, the tile grid covers the latent padded up to whole tiles (S' > S).
  *     Tile-major positions whose (t, h, w) coordinate lies outside the latent
  *     are padding: they are never keys, and O, LSE, dQ, dK and dV are written as
- *     zero there.  Their contents in q, k, v and dout must be finite
- *     (sta_tile_reorder writes zeros); they affect no other row.
+ *     zero there.  Their contents in q, k, v and dout may be any finite values
+ *     (sta_tile_reorder writes zeros): the kernels mask padding keys and
+ *     queries with selects, so even contents whose products overflow fp32
+ *     affect no other row.
  *   - Window of a head: (wt, wh, ww) in tiles, each >= 1.  Along a dimension with
  *     n tiles, w' = min(w, n) and the window of query tile q covers tiles
  *     [s, s + w') with s = clamp(q - floor(w'/2), 0, n - w'): the centre is

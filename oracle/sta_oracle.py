@@ -51,8 +51,8 @@ __all__ = [
     "tile_grid", "tile_major_index", "reorder", "unreorder", "padded_latent", "valid_positions",
     "pad_reorder", "pad_unreorder", "window_start",
     "window_contains", "tile_pairs", "token_tile_coords", "window_mask",
-    "forward", "backward", "backward_key_rows", "backward_query_rows", "dense_forward",
-    "window_mass",
+    "forward", "backward", "backward_key_rows", "backward_query_rows", "backward_key_rows_by_pairs",
+    "dense_forward", "window_mass",
 ]
 
 
@@ -380,6 +380,67 @@ def backward_key_rows(q, k, v, do, latent, tile, win, scale, b, h, key_rows, ord
         dk[~valid[key_rows]] = 0.0
         dv[~valid[key_rows]] = 0.0
     return dk, dv
+
+
+def backward_key_rows_by_pairs(q, k, v, do, latent, tile, win, scale, b, h, key_rows):
+    """dK and dV of one (batch b, head h) at tile-major key positions
+    ``key_rows``, written tile pair by tile pair.
+
+    [STA-meth]: each query tile attends densely to the key tiles of its
+    window.  This is the same gradient as ``backward``, organised the way the
+    method states it instead of as a masked dense matrix: for every query tile
+    a whose window holds a tile of the sampled keys, the keys of a's window
+    (its tiles, real positions only) give P = softmax(scale Q_a K_win^T),
+    O = P V_win and Dl = rowsum(dO_a * O); the sampled key columns j then get
+    dS_ij = P_ij (<dO_i, v_j> - Dl_i), dK_j += scale sum_i dS_ij q_i and
+    dV_j += sum_i P_ij dO_i.  Only the keys a query sees enter its softmax, so
+    the cost follows the window instead of the sequence (full-size samples of
+    the heaviest key tiles stay cheap).  fp64 torch CPU ops (multi-threaded).
+    """
+    import torch
+    grid = padded_latent(latent, tile)
+    n, L = tile_grid(grid, tile)
+    nt = n[0] * n[1] * n[2]
+    valid = valid_positions(latent, tile)
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    coords = _tile_coords(n)
+    win = tuple(int(x) for x in win)
+    # per query tile: the key tiles of its window
+    windows = [[t for t in range(nt) if window_contains(coords[a], coords[t], win, n)] for a in range(nt)]
+    ktiles = set(int(t) for t in np.unique(key_rows // L))
+    qf, kf, vf, dof = (torch.from_numpy(np.ascontiguousarray(a[b, h], dtype=np.float64)) for a in (q, k, v, do))
+    dk = torch.zeros((key_rows.size, qf.shape[1]), dtype=torch.float64)
+    dv = torch.zeros_like(dk)
+    pos = np.full(grid[0] * grid[1] * grid[2], -1, dtype=np.int64)
+    for a in range(nt):
+        if not ktiles.intersection(windows[a]):
+            continue
+        rows = np.arange(a * L, (a + 1) * L)
+        rows = rows[valid[rows]]                  # padding positions are no query
+        if rows.size == 0:
+            continue
+        cols = np.concatenate([np.arange(t * L, (t + 1) * L) for t in windows[a]])
+        cols = cols[valid[cols]]                  # ... and no key
+        pos[:] = -1
+        pos[cols] = np.arange(cols.size)
+        sel = np.flatnonzero(pos[key_rows] >= 0)  # sampled keys this query tile sees
+        if sel.size == 0:
+            continue
+        rt, ct = torch.from_numpy(rows), torch.from_numpy(cols)
+        qa, doa = qf[rt], dof[rt]
+        p = torch.softmax(scale * (qa @ kf[ct].T), dim=1)
+        o = p @ vf[ct]
+        dl = (doa * o).sum(dim=1, keepdim=True)
+        jt = torch.from_numpy(key_rows[sel])
+        pj = p[:, torch.from_numpy(pos[key_rows[sel]])]
+        ds = pj * (doa @ vf[jt].T - dl)
+        st = torch.from_numpy(sel)
+        dk[st] += scale * (ds.T @ qa)
+        dv[st] += pj.T @ doa
+    out_dk, out_dv = dk.numpy(), dv.numpy()
+    out_dk[~valid[key_rows]] = 0.0
+    out_dv[~valid[key_rows]] = 0.0
+    return out_dk, out_dv
 
 
 def backward_query_rows(q, k, v, do, latent, tile, win, scale, b, h, rows, order="tile"):

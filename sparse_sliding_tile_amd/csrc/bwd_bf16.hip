@@ -35,9 +35,8 @@ constexpr int kStage = 32;  // rows (keys or queries) per pipeline stage
 // --------------------------------------------------------------------------
 // 1. prep: Dl_i = <dO_i, O_i> (fp32) and lse2_i = LSE_i * log2(e).
 //    D/8 lanes per row, 16-byte loads, shuffle reduction.  Padding rows of a
-//    padded latent get lse2 = +inf and Dl = 0: with finite scores every P of
-//    such a query is then exactly zero, so the dK/dV passes need no query mask
-//    and dQ is zero there by construction.
+//    padded latent get lse2 = +inf and Dl = 0 (their P, dS and outputs are
+//    also masked by selects in the passes below).
 // --------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
@@ -252,17 +251,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
   // Padded latents: keys at padding positions of a partial key tile get
-  // P = 0 (a second walk over the key blocks, for the stage being computed).
+  // dS = 0 (a second walk over the key blocks, for the stage being computed).
   // The S^T accumulator holds key 8i + 4(l/32) + jj of the stage in element
   // 4i + jj: with w = 8 that is row 4 cjb + i of the tile and column
   // 4(l/32) + jj, so one bit per tile row (a ballot) and the tile's real width,
-  // worked out once per key tile, mask a stage by adding 0 or -inf (scores are
-  // finite, so the sum is exactly -inf).  PADM 2 tests every key of the block.
+  // worked out once per key tile, mask a stage.  The mask is a select on dS
+  // itself, so padding keys whose scores or dP overflow (any finite contents)
+  // still give exactly zero.  PADM 2 tests every key of the block.
   int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
   bool key_tile_partial = false, col_partial = false;
   uint64_t rows_real = ~0ull;  // bit R: tile row R is real
   int col_ext = 8;             // real columns of the key tile
-  auto mask_keys = [&](f32x16& st) {
+  auto mask_keys = [&](f32x16& x) {
     if constexpr (PADM == 0) return;
     const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
     if constexpr (PADM == 1) {
@@ -282,17 +282,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
         if (rb != 0xfu) {  // a row of the block is padding (uniform)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float rbias = (rb >> u) & 1u ? 0.f : -INFINITY;
+            const bool rreal = (rb >> u) & 1u;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) st[4 * u + jj] += rbias;
+            for (int jj = 0; jj < 4; ++jj) x[4 * u + jj] = rreal ? x[4 * u + jj] : 0.0f;
           }
         }
         if (col_partial) {
-          float cb[4];
+          bool creal[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) cb[jj] = 4 * grp + jj < col_ext ? 0.f : -INFINITY;
+          for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) st[e] += cb[e & 3];
+          for (int e = 0; e < 16; ++e) x[e] = creal[e & 3] ? x[e] : 0.0f;
         }
       }
     } else if (tile_partial(k0, k1, k2, g)) {
@@ -300,8 +300,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
       if (m != 0xffffffffu) {
         const uint32_t bits = lane_bits(m, lane);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (!elem_real(bits, e)) st[e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) x[e] = elem_real(bits, e) ? x[e] : 0.0f;
       }
     }
     if (++cjb == spt) {
@@ -321,8 +320,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     read_rows<D>(kl, kf, grp, c32);
     read_rows<D>(vl, vr, grp, c32);
     f32x16 st = contract_rows<D>(kf, qf);         // S^T[key][q]
-    mask_keys(st);
-    // a scheduling boundary after the mask (the dP^T reads stay below it:
+    // a scheduling boundary after S^T (the dP^T reads stay below it:
     // measured faster)
     __builtin_amdgcn_sched_barrier(0);
     f32x16 dpt;
@@ -331,14 +329,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
       read_rows<D>(dotile, dof, grp, c32);
       dpt = contract_rows<D>(vr, dof);              // dP^T[key][q]
     }
+    f32x16 dsf;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(st[e], c_log2, -lrow));
+      dsf[e] = p * (dpt[e] + ndrow);
+    }
+    mask_keys(dsf);
     bf16x8 ds[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * s + e], c_log2, -lrow));
-        ds[s][e] = (__bf16)(p * (dpt[8 * s + e] + ndrow));
-      }
+      for (int e = 0; e < 8; ++e) ds[s][e] = (__bf16)dsf[8 * s + e];
     bf16x8 ktf[DT][2];
     read_cols<D>(kl, ktf, lane);
 #pragma unroll
@@ -376,14 +378,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj; zero
   // on padding rows.
   const int rin = sub * (NW * 32) + wave * 32 + c32;  // row inside the query tile
-  const float osc = (!g.padded || token_real(a0, a1, a2, rin, g)) ? scale : 0.0f;
+  const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x4 w;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(acc[dt][4 * i + jj] * osc);
+      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(real ? acc[dt][4 * i + jj] * scale : 0.0f);
       *(bf16x4*)(dq + row * D + dt * 32 + 8 * i + 4 * grp) = w;
     }
 }
@@ -405,7 +407,8 @@ __device__ __forceinline__ void dma_stats(const float* __restrict__ lse2, const 
 // MODE 0 computes dV (S = Q K^T, P, dV += P^T dO); MODE 1 computes dK
 // (S, dP = dO V^T, dS, dK += dS^T Q).  Two launches instead of one keep the
 // resident state of each under the register file (one fused kernel spills).
-template <int D, int NW, int MODE, int OCC>
+// PADM as in the dQ pass, here for the query rows of partial query tiles.
+template <int D, int NW, int MODE, int OCC, int PADM>
 __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
@@ -482,8 +485,72 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  // Padding queries of a padded latent need no mask here: their lse2 is +inf,
-  // so their P (and dS) is exactly zero.
+  // Padded latents: the P (dV) or dS (dK) operand of padding query rows of a
+  // partial query tile is set to zero with a select, so any finite padding
+  // contents (even ones whose scores or dP overflow) contribute nothing.  A
+  // second walk over the query blocks follows the stage being computed.
+  // Element 4i + jj of the S accumulator holds query 8i + 4(l/32) + jj of the
+  // stage: with w = 8 that is row 4 cjb + i of the tile and column
+  // 4(l/32) + jj, so one bit per tile row (a ballot) and the tile's real width
+  // are worked out once per query tile (PADM 1); PADM 2 tests every query of
+  // the block.
+  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  bool qtile_partial = false, col_partial = false;
+  uint64_t rows_real = ~0ull;  // bit R: tile row R is real
+  int col_ext = 8;             // real columns of the query tile
+  auto mask_queries = [&](float (&x)[16]) {
+    if constexpr (PADM == 0) return;
+    const int t0 = lo0 + ci0, t1 = lo1 + ci1, t2 = lo2 + ci2;
+    if constexpr (PADM == 1) {
+      if (cjb == 0) {  // a new query tile
+        qtile_partial = tile_partial(t0, t1, t2, g);
+        if (qtile_partial) {
+          const int e0 = tile_ext(t0, g.t, g.T), e1 = tile_ext(t1, g.h, g.H), e2 = tile_ext(t2, g.w, g.W);
+          const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
+          const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
+          rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
+          col_ext = e2;
+          col_partial = e2 < 8;
+        }
+      }
+      if (qtile_partial) {
+        const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
+        if (rb != 0xfu) {  // a row of the block is padding (uniform)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool rreal = (rb >> u) & 1u;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) x[4 * u + jj] = rreal ? x[4 * u + jj] : 0.0f;
+          }
+        }
+        if (col_partial) {
+          bool creal[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[e] = creal[e & 3] ? x[e] : 0.0f;
+        }
+      }
+    } else if (tile_partial(t0, t1, t2, g)) {
+      const uint32_t m = block_real_mask(t0, t1, t2, cjb * kStage, g, lane);
+      if (m != 0xffffffffu) {
+        const uint32_t bits = lane_bits(m, lane);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = elem_real(bits, e) ? x[e] : 0.0f;
+      }
+    }
+    if (++cjb == spt) {
+      cjb = 0;
+      if (++ci2 == c2) {
+        ci2 = 0;
+        if (++ci1 == c1) {
+          ci1 = 0;
+          ++ci0;
+        }
+      }
+    }
+  };
+
   auto step = [&](const char* ql, const char* dol, const char* st) {
     f32x16 s, dp;
     {
@@ -522,6 +589,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
         pe[e] = MODE == 0 ? p : p * dp[e];
       }
     }
+    mask_queries(pe);
     // the second GEMM's operand reads start after the exponentials (measured
     // faster for dV than the compiler's interleave; dK is indifferent)
     __builtin_amdgcn_sched_barrier(0);
@@ -616,13 +684,20 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   else if (g.w == 8 && g.t * g.h <= 64) dq_pass(std::integral_constant<int, 1>{});
   else dq_pass(std::integral_constant<int, 2>{});
   // dV asks for two waves per SIMD, except one-wave workgroups at D = 128,
-  // whose registers allow one.
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, (NW >= 2 || D <= 64) ? 2 : 1>), dim3((uint32_t)total),
-                     dim3(64 * NW), 0, st, q,
-                     k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
-  // dK fits two waves per SIMD in 4-wave workgroups; smaller ones keep one.
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, NW >= 4 ? 2 : 1>), dim3((uint32_t)total), dim3(64 * NW), 0, st, q,
-                     k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
+  // whose registers allow one; dK fits two waves per SIMD in 4-wave
+  // workgroups, smaller ones keep one.
+  auto dkv_pass = [&](auto padm) {
+    constexpr int PADM = decltype(padm)::value;
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 0, (NW >= 2 || D <= 64) ? 2 : 1, PADM>),
+                       dim3((uint32_t)total), dim3(64 * NW), 0, st, q, k, v, dout, lse2, dl, dk, dv,
+                       rank_tab, g, ht, B, Hh, c_log2, scale, bpt);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, 1, NW >= 4 ? 2 : 1, PADM>), dim3((uint32_t)total),
+                       dim3(64 * NW), 0, st, q, k, v, dout, lse2, dl, dk, dv, rank_tab, g, ht, B, Hh,
+                       c_log2, scale, bpt);
+  };
+  if (!g.padded) dkv_pass(std::integral_constant<int, 0>{});
+  else if (g.w == 8 && g.t * g.h <= 64) dkv_pass(std::integral_constant<int, 1>{});
+  else dkv_pass(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 

@@ -336,8 +336,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // the S^T accumulator holds row e / 4 of the block and column 4 (l / 32) +
   // e % 4 of the tile.  A key is real when its row (i0, i1) and its column
   // are: one bit per tile row (a ballot) and the tile's real width are worked
-  // out once per key tile, and a stage adds 0 or -inf to the scores of padding
-  // rows and columns (scores are finite, so the sum is exactly -inf).
+  // out once per key tile, and a stage sets the scores of padding rows and
+  // columns to -inf (a select, so any finite padding contents, even ones whose
+  // products overflow, are masked exactly).
   // PADM 2 tests every key of the block (ballot per stage).
   constexpr bool row_col_mask = PADM == 1;
   bool key_tile_partial = false, col_partial = false;
@@ -377,21 +378,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         if (rb != 0xfu) {  // a row of the block is padding (uniform)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float rbias = (rb >> u) & 1u ? 0.f : -INFINITY;
+            const bool rreal = (rb >> u) & 1u;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) sacc[qt][4 * u + jj] += rbias;
+              for (int jj = 0; jj < 4; ++jj)
+                sacc[qt][4 * u + jj] = rreal ? sacc[qt][4 * u + jj] : -INFINITY;
           }
         }
-        if (col_partial) {  // scores are finite, so adding -inf masks exactly
-          float cb[4];
+        if (col_partial) {
+          bool creal[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) cb[jj] = 4 * grp + jj < col_ext ? 0.f : -INFINITY;
+          for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[qt][e] += cb[e & 3];
+            for (int e = 0; e < 16; ++e) sacc[qt][e] = creal[e & 3] ? sacc[qt][e] : -INFINITY;
         }
       }
     } else if (PADM == 2 && tile_partial(k0, k1, k2, g)) {
@@ -536,13 +538,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow[qt];
     if constexpr (!MASS) {
+      // padding rows: a select, not a product (their sums need not be finite)
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bf16x4 w;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qt][dt][4 * i + j] * inv);
+          for (int j = 0; j < 4; ++j) w[j] = (__bf16)(real ? oacc[qt][dt][4 * i + j] * inv : 0.0f);
           *(bf16x4*)(o + row * D + dt * 32 + 8 * i + 4 * grp) = w;
         }
     } else {
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       for (int c = 0; c < kMaxCandidates; ++c) {
         if (c < ma.ncand) {
           const float lcs = xsum32(lcand[qt][c]);
-          float r = lcs * inv;  // 0 on padding rows
+          float r = real ? lcs * inv : 0.0f;  // a select: 0 on padding rows
           // sum over the 32 rows (lanes 0..31; lanes 32..63 hold the same rows)
 #pragma unroll
           for (int off = 16; off > 0; off >>= 1) r += __shfl_xor(r, off, 32);

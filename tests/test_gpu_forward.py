@@ -168,6 +168,36 @@ def test_forward_raster_hunyuan_bit_identical(sta):
     assert torch.equal(lr.view(torch.int32), lse.view(torch.int32))
 
 
+def test_forward_raster_bench_config_sampled(sta):
+    """The benchmark's step itself, in its launch configuration:
+    sta_forward_raster on the (30,48,80) latent, tile (6,8,8), 24 heads,
+    D = 128, window (3,3,3), on the benchmark's seeded inputs.  Sampled raster
+    rows (corners of the latent, tile-boundary rows and seeded random rows) of
+    three heads against the oracle in raster order."""
+    name = "hunyuan_30x48x80_w333"
+    w = I.WORKLOADS[name]
+    latent, tile, wins, D = w["latent"], w["tile"], w["windows"], w["head_dim"]
+    T, H, W = latent
+    S = T * H * W
+    print(f"[raster bench config] {name}", flush=True)
+    x = I.workload_inputs(name)
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sta.forward_raster(q, k, v, latent, tile, wins)
+    torch.cuda.synchronize()
+    corners = [((a * H) + b) * W + c for a in (0, T - 1) for b in (0, H - 1) for c in (0, W - 1)]
+    edges = [((5 * H) + 7) * W + 8, ((6 * H) + 8) * W + 7, ((17 * H) + 23) * W + 40]   # tile borders
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([corners, edges, rng.integers(0, S, 120)]))
+    rt = torch.from_numpy(rows).cuda()
+    for h in (0, 12, 23):
+        ro, rl = O.forward(*(to64(x[nm][:, h:h + 1]) for nm in ("q", "k", "v")), latent, tile, [wins[h]],
+                           D ** -0.5, order="raster", rows=rows)
+        eo, el = err_report(to64(o[:, h:h + 1, rt]), ro), err_report(to64(lse[:, h:h + 1, rt]), rl)
+        print("head", h, "O", eo, "LSE", el)
+        assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+        assert el["max_abs"] < BF16_TOL
+
+
 BF16_SMALL = [  # latent, tile, B, windows, D   (tile volume 32 and 128; several tiles; batch 2)
     ((6, 16, 16), (2, 4, 4), 2, [(3, 3, 3), (1, 2, 5), (9, 9, 9)], 128),
     ((6, 16, 16), (2, 4, 4), 1, [(2, 3, 1), (3, 1, 3)], 64),

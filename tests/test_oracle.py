@@ -697,3 +697,31 @@ def test_window_mass_grows_with_nested_windows():
     m = O.window_mass(q, k, latent, tile, [(1, 1, 1), (3, 1, 1), (3, 1, 3), (5, 2, 3)], 1.0)
     assert np.all(np.diff(m[:, 0, :], axis=0) > 0)
     np.testing.assert_allclose(m[-1], 1.0, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- pair-by-pair key rows
+
+@pytest.mark.parametrize("latent,tile,win", [
+    ((6, 16, 16), (2, 4, 4), (3, 3, 3)),
+    ((6, 16, 16), (2, 4, 4), (2, 1, 4)),          # even windows, one of them clamped
+    ((6, 16, 16), (2, 4, 4), (9, 9, 9)),          # full window
+    ((5, 15, 13), (2, 4, 4), (3, 1, 3)),          # padded to (6, 16, 16)
+])
+def test_backward_key_rows_by_pairs_matches_full(latent, tile, win):
+    """The pair-by-pair formulation equals the masked dense backward at every
+    sampled key row, heaviest and padding rows included."""
+    S = O.tile_grid(O.padded_latent(latent, tile), tile)[1] * int(np.prod(
+        [-(-a // b) for a, b in zip(latent, tile)]))
+    q, k, v, do = (_rand((1, 2, S, 8), s) for s in (80, 81, 82, 83))
+    valid = O.valid_positions(latent, tile)
+    for a in (q, k, v, do):
+        a[:, :, ~valid] = 0.0
+    _, dk, dv = O.backward(q, k, v, do, latent, tile, [win, win], 0.4)
+    rows = np.array([0, 1, 31, 32, 300, 777, 1000, S - 33, S - 1])
+    dk2, dv2 = O.backward_key_rows_by_pairs(q, k, v, do, latent, tile, win, 0.4, 0, 1, rows)
+    np.testing.assert_allclose(dk2, dk[0, 1, rows], atol=1e-12)
+    np.testing.assert_allclose(dv2, dv[0, 1, rows], atol=1e-12)
+    # and the masked dense helper agrees too
+    dk3, dv3 = O.backward_key_rows(q, k, v, do, latent, tile, win, 0.4, 0, 1, rows)
+    np.testing.assert_allclose(dk2, dk3, atol=1e-12)
+    np.testing.assert_allclose(dv2, dv3, atol=1e-12)
