@@ -45,7 +45,8 @@
  *     launches are asynchronous: a return of STA_OK means the work was queued.
  *   - Return value: STA_OK (0) or a negative STA_ERR_* code.  Every argument is
  *     validated before anything is launched; on an error nothing is launched and
- *     no output is touched.  There is no mutable global state: calls are
+ *     no output is touched.  The only mutable global state is the static
+ *     scratch of sta_backward_noalloc (see there); every other call is
  *     thread-safe; calls that write the same buffers must be ordered by the caller.
  */
 #ifndef STA_H_
@@ -85,6 +86,7 @@ enum {
 
 #define STA_MAX_HEADS 256
 #define STA_MAX_CANDIDATES 8 /* candidate windows per sta_window_mass call */
+#define STA_NOALLOC_SCRATCH_BYTES (32u << 20) /* static scratch of sta_backward_noalloc */
 
 /* Human-readable text for a return code (static storage). */
 const char* sta_strerror(int code);
@@ -171,6 +173,27 @@ int sta_backward(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                  int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
                  const int32_t* win_host, float scale, sta_dtype dt, void* stream);
+
+/* sta_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the workspace replaced by a static
+ * device array of STA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds
+ * on each GPU it runs on until the process ends.  It calls no hipMalloc,
+ * hipFree or other allocating routine.  Arguments as sta_backward, without
+ * workspace and ws_bytes; sizes whose workspace
+ * (sta_backward_workspace_bytes) exceeds the array are refused with
+ * STA_ERR_TOO_LARGE before anything is launched (2*B*Hh*S' fp32 row
+ * statistics plus the bf16 path's key-tile order must fit: about 4.19 M
+ * tile-major rows over all (b, head)).  The first call on a device looks the
+ * array's address up (hipGetSymbolAddress); STA_ERR_HIP if that fails.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, or several host threads) race and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero:
+ * every value the kernels read from it is written earlier in the same call. */
+int sta_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                         const int32_t* win_host, float scale, sta_dtype dt, void* stream);
 
 /* Dense softmax attention over all S keys: the full-attention baseline STA is
  * compared with ([STA-abs] compares with FlashAttention).  Same kernel family

@@ -39,6 +39,8 @@ SIGNATURES = {
     "sta_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int]),
     "sta_backward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                     c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
+    "sta_backward_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                            c_i64, c_i64, c_i64, Dim3, Dim3, c_vp, c_f32, ctypes.c_int, c_vp]),
     "sta_dense_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
                                          c_f32, ctypes.c_int, c_vp]),
     "sta_window_mass_workspace_bytes": (c_sz, [c_i64, c_i64, Dim3, Dim3, c_i64]),
@@ -264,6 +266,27 @@ def backward(q, k, v, o, do, lse, latent, tile, windows, scale=None, workspace=N
                               _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                               B, Hh, D, _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale,
                               _dtype(q), _stream(q)), "sta_backward")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, latent, tile, windows, scale=None, out=None):
+    """STA backward through sta_backward_noalloc (the library's static scratch
+    instead of a workspace): returns (dQ, dK, dV).  ``out`` may pass the three
+    output tensors, so the call itself allocates nothing."""
+    B, Hh, S, D = _shape4(q, "q")
+    if S != tile_major_len(latent, tile):
+        raise ValueError(f"q has {S} rows, tile-major {latent}/{tile} has {tile_major_len(latent, tile)}")
+    _same(q.shape, "q", ("q", q), ("k", k), ("v", v), ("o", o), ("do", do))
+    if tuple(lse.shape) != (B, Hh, S) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hh, S]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    w = _windows(windows, Hh)
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None else out
+    _same(q.shape, "q", ("dq", dq), ("dk", dk), ("dv", dv))
+    _check(lib().sta_backward_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(do, "do"),
+                                      _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"),
+                                      B, Hh, D, _dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), scale,
+                                      _dtype(q), _stream(q)), "sta_backward_noalloc")
     return dq, dk, dv
 
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -273,6 +274,66 @@ int sta_backward(const void* q, const void* k, const void* v, const void* o, con
                                     (int)Hh, (int)D, scale, s));
   }
   return STA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Static scratch for sta_backward_noalloc.  Each GPU the library runs on holds
+// its own copy of this array until the process ends.  In host code the name
+// is only a stand-in: the device address of a GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device and
+// kept in noalloc_scratch[].
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[STA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag noalloc_once[kMaxDevices];
+void* noalloc_scratch[kMaxDevices];
+hipError_t noalloc_status[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr (with *err set).
+void* scratch_for_current_device(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(noalloc_once[dev], [dev]() {
+    void* ptr = nullptr;
+    noalloc_status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    noalloc_scratch[dev] = noalloc_status[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *err = noalloc_status[dev];
+  return noalloc_scratch[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int sta_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
+                         const int32_t* win_host, float scale, sta_dtype dt, void* stream) {
+  // Every argument check of sta_backward runs first (with the workspace
+  // replaced by the static array), so a rejected call touches no device.
+  Geometry g;
+  HeadTable ht;
+  int st = make_geometry(latent, tile, &g);
+  if (st) return st;
+  if ((st = make_heads(win_host, Hh, g, &ht))) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
+  if ((st = check_sizes(B, Hh, D, g))) return st;
+  const size_t need = sta_backward_workspace_bytes(B, Hh, D, latent, tile, dt);
+  if (need == 0 || need > (size_t)STA_NOALLOC_SCRATCH_BYTES) return STA_ERR_TOO_LARGE;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_for_current_device(&e);
+  if (ws == nullptr) return STA_ERR_HIP;
+  return sta_backward(q, k, v, o, dout, lse, dq, dk, dv, ws, need, B, Hh, D, latent, tile, win_host,
+                      scale, dt, stream);
 }
 
 int sta_dense_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

@@ -150,6 +150,30 @@ def test_backward_argument_errors(lib):
     assert bwd(windows=NUL) == ARG
 
 
+def test_backward_noalloc_argument_errors(lib):
+    """The static-scratch backward validates everything before it touches a
+    device: bad arguments and sizes whose workspace exceeds the 32 MiB array."""
+    w = win([(3, 3, 3)] * 2)
+    wp = w.ctypes.data_as(ctypes.c_void_p)
+
+    def bn(lse=P, dq=P, B=1, Hh=2, D=128, latent=(6, 16, 16), tile=(2, 4, 4), windows=wp, scale=0.1, dt=0):
+        return lib.sta_backward_noalloc(P, P, P, P, P, lse, dq, P, P, B, Hh, D, d3(*latent), d3(*tile), windows,
+                                        scale, dt, NUL)
+    assert bn(lse=NUL) == ARG
+    assert bn(dq=NUL) == ARG
+    assert bn(scale=0.0) == ARG
+    assert bn(windows=NUL) == ARG
+    assert bn(latent=(0, 16, 16)) == ARG
+    # 40 heads at (30, 48, 80): 8 bytes of row statistics per row, 4.6 M rows > 32 MiB
+    forty = win([(3, 3, 3)] * 40)
+    assert bn(Hh=40, latent=(30, 48, 80), tile=(6, 8, 8), windows=forty.ctypes.data_as(ctypes.c_void_p)) == TOO_LARGE
+    need = lib.sta_backward_workspace_bytes(1, 40, 128, d3(30, 48, 80), d3(6, 8, 8), 0)
+    assert need > (32 << 20)
+    # the fine-tuning and HunyuanVideo shapes at 24 heads fit
+    assert lib.sta_backward_workspace_bytes(1, 24, 128, d3(24, 64, 64), d3(6, 8, 8), 0) <= (32 << 20)
+    assert lib.sta_backward_workspace_bytes(1, 24, 128, d3(30, 48, 80), d3(6, 8, 8), 0) <= (32 << 20)
+
+
 def test_dense_argument_errors(lib):
     f = lib.sta_dense_forward
     assert f(P, P, P, P, NUL, 1, 2, 1000, 128, 0.1, 0, NUL) == UNSUP    # bf16 needs S % 32 == 0
