@@ -66,6 +66,30 @@ def fwd_flops(latent, tile, windows, batch, head_dim):
     return sum(batch * nt * kh(w, n) * 4 * L * L * head_dim for w in windows)
 
 
+def real_token_flops(latent, tile, windows, batch, head_dim):
+    """Counted forward FLOP over real tokens only: for every computed (query
+    tile, key tile) pair, 4 * D * (real queries of the one) * (real keys of the
+    other).  Equal to fwd_flops for a latent of whole tiles."""
+    n = [-(-a // b) for a, b in zip(latent, tile)]
+    ext = [[min(t_, a - i * t_) for i in range(m)] for a, t_, m in zip(latent, tile, n)]
+
+    def start(q, w, m):
+        wp = min(w, m)
+        return min(max(q - wp // 2, 0), m - wp), wp
+    total = 0
+    for w in windows:
+        # per dimension: sum over query tiles of real(q) * sum of real(k) in its window
+        per_dim = []
+        for d in range(3):
+            acc = 0
+            for qi in range(n[d]):
+                s0, wp = start(qi, w[d], n[d])
+                acc += ext[d][qi] * sum(ext[d][s0:s0 + wp])
+            per_dim.append(acc)
+        total += batch * 4 * head_dim * per_dim[0] * per_dim[1] * per_dim[2]
+    return total
+
+
 class Timer:
     """Events on the current stream (the stream libsta launches on)."""
 
@@ -105,7 +129,9 @@ def source_hash(paths=None):
 
 def read_traffic():
     """HBM bytes per sta_forward launch from the committed rocprofv3 counter
-    summary, or None when it is missing or the kernel source changed since."""
+    summary, and where that figure comes from; the bytes are None when the
+    file is missing or the kernel's code changed since it was measured."""
+    rel = os.path.relpath(TRAFFIC_FILE, ROOT)
     try:
         vals = {}
         with open(TRAFFIC_FILE) as f:
@@ -113,11 +139,15 @@ def read_traffic():
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     vals[k.strip()] = v.strip()
-        if vals.get("source_sha256_16") != source_hash():
-            return None
-        return float(vals["hbm_bytes_per_launch"])
+        measured, current = vals.get("source_sha256_16"), source_hash()
+        if measured != current:
+            return None, (f"null: {rel} was measured on kernel code {measured}, the code now hashes to "
+                          f"{current}")
+        return float(vals["hbm_bytes_per_launch"]), (
+            f"{rel} (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this bench, scaled by a copy of known "
+            f"size; kernel code hash {measured}, the code this run executes)")
     except (OSError, KeyError, ValueError):
-        return None
+        return None, f"null: {rel} missing or unreadable"
 
 
 def cpu_baseline(x, latent, tile, window, head_dim, target_s):
@@ -144,6 +174,7 @@ def cpu_baseline(x, latent, tile, window, head_dim, target_s):
     flops = done * kh(window, n) * 4 * L * L * head_dim
     nt, heads = n[0] * n[1] * n[2], x["q"].shape[1]
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "blas_threads": threads, "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
             "s_per_query_tile": round(el / done, 4),
             "extrapolated_s_per_launch": round(el / done * nt * heads, 1),  # x tiles x heads, extrapolated
             "sample": f"{done} query tiles ({done * L} rows) of head 0 of 24, all {L * n[0] * n[1] * n[2]} keys "
@@ -152,6 +183,15 @@ def cpu_baseline(x, latent, tile, window, head_dim, target_s):
 
 
 def cpu_model():
+    """The host CPU's model string (lscpu, else /proc/cpuinfo)."""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -224,7 +264,7 @@ def main():
     log(f"[bench] step {ms_step:.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms), forward kernel {fwd_ms:.3f} ms")
     achieved = flops / (fwd_ms * 1e-3) / 1e12
     each = fwd_timer.each_ms()   # per-step times of the same timed steps
-    traffic = read_traffic()
+    traffic, traffic_source = read_traffic()
     result = {
         "metric": "effective TFLOP/s and % bf16 MFMA peak, STA fwd at (30,48,80) latent",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -246,7 +286,8 @@ def main():
                    "step_ms_median": round(each[len(each) // 2], 4), "step_ms_min": round(each[0], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "sta_forward_raster (fwd_bf16_kernel, raster instance)",
+                     "traffic": traffic, "traffic_source": traffic_source,
+                     "kernel": "sta_forward_raster (fwd_bf16_kernel, raster instance)",
                      "kernel_ms": round(fwd_ms, 4), "flops_per_launch": flops},
     }
 
@@ -299,13 +340,52 @@ def main():
         r_ms = rt.total_ms() / 5
         nbytes = 2 * q.numel() * q.element_size()
         legs["tile_reorder"] = {"ms": round(r_ms, 4), "GB/s": round(nbytes / r_ms / 1e6, 1),
-                                "frac_of_hbm_peak": round(nbytes / r_ms / 1e6 / PEAK_HBM_GBS, 3)}
+                                "frac_of_hbm_peak": round(nbytes / r_ms / 1e6 / PEAK_HBM_GBS, 3),
+                                "tensor": list(q.shape)}
+        ut = Timer(torch)
+        for _ in range(5):
+            with ut:
+                sta.tile_unreorder(ot, latent, tile, out=o)
+        torch.cuda.synchronize()
+        u_ms = ut.total_ms() / 5
+        legs["tile_unreorder"] = {"ms": round(u_ms, 4), "GB/s": round(nbytes / u_ms / 1e6, 1),
+                                  "frac_of_hbm_peak": round(nbytes / u_ms / 1e6 / PEAK_HBM_GBS, 3),
+                                  "tensor": list(q.shape)}
         del x, q, k, v, qt, kt, vt, ot, o, lse
         torch.cuda.empty_cache()
         g = torch.Generator(device=dev).manual_seed(1)
 
         def rand(shape):
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        # reorder / unreorder round trip at the Wan shape (24,48,80), 40 heads:
+        # each an HBM-bound copy (read + write of one tensor)
+        ww = I.WORKLOADS["wan_24x48x80_w335"]
+        wshape = (ww["batch"], ww["heads"], sta.raster_len(ww["latent"]), ww["head_dim"])
+        xr = rand(wshape)
+        xt, xb = torch.empty_like(xr), torch.empty_like(xr)
+        sta.tile_reorder(xr, ww["latent"], ww["tile"], out=xt)
+        sta.tile_unreorder(xt, ww["latent"], ww["tile"], out=xb)
+        tr, tu, trt = Timer(torch), Timer(torch), Timer(torch)
+        for _ in range(5):
+            with trt:
+                with tr:
+                    sta.tile_reorder(xr, ww["latent"], ww["tile"], out=xt)
+                with tu:
+                    sta.tile_unreorder(xt, ww["latent"], ww["tile"], out=xb)
+        torch.cuda.synchronize()
+        wbytes = 2 * xr.numel() * xr.element_size()
+        rt_ok = bool(torch.equal(xb.view(torch.int16), xr.view(torch.int16)))
+        legs["wan_reorder_round_trip"] = {
+            "tensor": list(wshape), "bytes_per_copy": wbytes,
+            "reorder_ms": round(tr.total_ms() / 5, 4), "reorder_GB/s": round(wbytes / (tr.total_ms() / 5) / 1e6, 1),
+            "unreorder_ms": round(tu.total_ms() / 5, 4),
+            "unreorder_GB/s": round(wbytes / (tu.total_ms() / 5) / 1e6, 1),
+            "round_trip_ms": round(trt.total_ms() / 5, 4),
+            "round_trip_GB/s": round(2 * wbytes / (trt.total_ms() / 5) / 1e6, 1),
+            "frac_of_hbm_peak": round(2 * wbytes / (trt.total_ms() / 5) / 1e6 / PEAK_HBM_GBS, 3),
+            "round_trip_bit_exact": rt_ok}
+        del xr, xt, xb
 
         for lname in ("hunyuan_30x48x80_mixed", "wan_24x48x80_w335", "image_2d_1x128x128_w155",
                       "hunyuan_29x45x76_w333_padded"):
@@ -325,6 +405,12 @@ def main():
             lf = fwd_flops(lw["latent"], lw["tile"], lw["windows"], lw["batch"], lw["head_dim"])
             legs[lname] = {"ms": round(lms, 3), "tflops": round(lf / lms / 1e9, 1),
                            "pct_of_peak": round(100 * lf / lms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+            if lname.endswith("padded"):
+                rf = real_token_flops(lw["latent"], lw["tile"], lw["windows"], lw["batch"], lw["head_dim"])
+                legs[lname].update({"counted": "tflops over the padded tile grid", "real_token_tflops":
+                                    round(rf / lms / 1e9, 1), "real_token_pct_of_peak":
+                                    round(100 * rf / lms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                                    "real_token_share_of_counted": round(rf / lf, 4)})
             if lname.endswith("mixed"):
                 legs[lname]["windows"] = [list(x_) for x_ in lw["windows"]]
             del a, b_, c, out, ll
@@ -350,6 +436,9 @@ def main():
             legs[bname + "_backward"] = {
                 "ms": round(bms, 3), "tflops": round(bflops / bms / 1e9, 1),
                 "pct_of_peak": round(100 * bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                "real_token_pct_of_peak": round(
+                    100 * real_token_flops(fw["latent"], fw["tile"], fw["windows"], fw["batch"], fw["head_dim"])
+                    * 10 // 4 / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "counted": "10*L^2*D per tile pair (5 GEMMs, padded grid for a padded latent); the kernels run 8 (dQ, dV and dK passes)"}
             del a, b_, c, do, out, ll, ws
         # window search, measurement side: attention mass of the five

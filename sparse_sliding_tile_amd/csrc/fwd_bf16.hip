@@ -330,6 +330,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
   bool tile_done = false;
   uint32_t member = 0;
+  // Mass instance: the start of every candidate window of this query tile
+  // (fixed for the whole walk).
+  int cs[MASS ? kMaxCandidates : 1][3];
+  if constexpr (MASS) {
+#pragma unroll
+    for (int c = 0; c < kMaxCandidates; ++c) {
+      const bool use = c < ma.ncand;
+      cs[c][0] = use ? window_start(a0, ma.w[c][0], g.n0) : 0;
+      cs[c][1] = use ? window_start(a1, ma.w[c][1], g.n1) : 0;
+      cs[c][2] = use ? window_start(a2, ma.w[c][2], g.n2) : 0;
+    }
+  }
   // Padding masks (PADM, one instance each): 0 whole-tile latent, no mask;
   // 1 tiles 8 keys wide with at most 64 tile rows; 2 any other tile.
   // PADM 1: a 32-key block is 4 tile rows of 8, and element e of lane l in
@@ -360,15 +372,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
     if constexpr (MASS) {
       tile_done = cjb == bpt - 1;
-      member = 0;
+      if (cjb == 0) {  // a new key tile: which candidate windows hold it
+        member = 0;
 #pragma unroll
-      for (int c = 0; c < kMaxCandidates; ++c) {
-        if (c < ma.ncand) {
-          const int cw0 = ma.w[c][0], cw1 = ma.w[c][1], cw2 = ma.w[c][2];
-          const bool in = (unsigned)(k0 - window_start(a0, cw0, g.n0)) < (unsigned)cw0 &&
-                          (unsigned)(k1 - window_start(a1, cw1, g.n1)) < (unsigned)cw1 &&
-                          (unsigned)(k2 - window_start(a2, cw2, g.n2)) < (unsigned)cw2;
-          member |= (in ? 1u : 0u) << c;
+        for (int c = 0; c < kMaxCandidates; ++c) {
+          if (c < ma.ncand) {
+            const bool in = (unsigned)(k0 - cs[c][0]) < (unsigned)ma.w[c][0] &&
+                            (unsigned)(k1 - cs[c][1]) < (unsigned)ma.w[c][1] &&
+                            (unsigned)(k2 - cs[c][2]) < (unsigned)ma.w[c][2];
+            member |= (in ? 1u : 0u) << c;
+          }
         }
       }
     }
