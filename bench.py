@@ -411,6 +411,27 @@ def main():
                                     round(rf / lms / 1e9, 1), "real_token_pct_of_peak":
                                     round(100 * rf / lms / 1e9 / PEAK_BF16_TFLOPS, 2),
                                     "real_token_share_of_counted": round(rf / lf, 4)})
+                # the padded step in one launch on raster tensors of the real
+                # tokens (no reorder kernels), against the whole-tile step
+                rshape = (lw["batch"], lw["heads"], sta.raster_len(lw["latent"]), lw["head_dim"])
+                ra, rb, rc = rand(rshape), rand(rshape), rand(rshape)
+                rout = torch.empty_like(ra)
+                rl = torch.empty(rshape[:3], dtype=torch.float32, device=dev)
+                sta.forward_raster(ra, rb, rc, lw["latent"], lw["tile"], lw["windows"], out=rout, lse=rl)
+                rtm = Timer(torch)
+                for _ in range(5):
+                    with rtm:
+                        sta.forward_raster(ra, rb, rc, lw["latent"], lw["tile"], lw["windows"], out=rout, lse=rl)
+                torch.cuda.synchronize()
+                rms = rtm.total_ms() / 5
+                legs[lname + "_raster_step"] = {
+                    "ms": round(rms, 3), "tflops": round(lf / rms / 1e9, 1),
+                    "pct_of_peak": round(100 * lf / rms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                    "real_token_pct_of_peak": round(100 * rf / rms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                    "over_whole_tile_step": round(rms / ms_step, 4),
+                    "note": "sta_forward_raster, one launch, raster tensors of the real tokens; "
+                            "over_whole_tile_step = this time / the (30,48,80) bench step"}
+                del ra, rb, rc, rout, rl
             if lname.endswith("mixed"):
                 legs[lname]["windows"] = [list(x_) for x_ in lw["windows"]]
             del a, b_, c, out, ll

@@ -74,7 +74,7 @@ typedef enum { STA_BF16 = 0, STA_F32 = 1 } sta_dtype;
 enum {
   STA_OK = 0,
   STA_ERR_ARG = -1,               /* null pointer, non-positive size, bad scale */
-  STA_ERR_NOT_TILE_MULTIPLE = -2, /* sta_forward_raster only: the other calls pad with masking */
+  STA_ERR_NOT_TILE_MULTIPLE = -2, /* reserved: every call pads such latents with masking */
   STA_ERR_WINDOW = -3,            /* a window entry < 1 */
   STA_ERR_UNSUPPORTED = -4,       /* head_dim, tile volume or dtype not built */
   STA_ERR_ALIGN = -5,             /* a tensor pointer not 16-byte aligned */
@@ -143,11 +143,13 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
  * one launch replaces reorder x3 + sta_forward + unreorder with the same
  * arithmetic in the same order (outputs bit-identical to that sequence).
  * q, k, v, o: bf16 [B, Hh, T*H*W, D] in raster order (W fastest); lse: fp32
- * [B, Hh, T*H*W] raster or NULL.  Needs a whole-tile latent
- * (STA_ERR_NOT_TILE_MULTIPLE otherwise; use the reorder path for padding),
- * STA_BF16 with D in {64, 128}, L % 32 == 0, the tile width a multiple of
- * 512 / D and L <= 1024 * 512 / D, i.e. 4096 tokens for D = 128 and 8192 for
- * D = 64 (STA_ERR_UNSUPPORTED otherwise).  Other arguments as sta_forward. */
+ * [B, Hh, T*H*W] raster or NULL.  A latent that is not a whole number of
+ * tiles is padded with masking as in sta_forward: the raster tensors hold
+ * only the T*H*W real tokens (padding positions have no rows, are never
+ * keys and produce no output).  Needs STA_BF16 with D in {64, 128},
+ * L % 32 == 0, the tile width a multiple of 512 / D and
+ * L <= 1024 * 512 / D, i.e. 4096 tokens for D = 128 and 8192 for D = 64
+ * (STA_ERR_UNSUPPORTED otherwise).  Other arguments as sta_forward. */
 int sta_forward_raster(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
                        const int32_t* win_host, float scale, sta_dtype dt, void* stream);

@@ -219,7 +219,6 @@ int sta_forward_raster(const void* q, const void* k, const void* v, void* o, flo
   if (!q || !k || !v || !o) return STA_ERR_ARG;
   if (!(scale > 0.f) || !(scale < INFINITY)) return STA_ERR_ARG;
   if ((st = check_sizes(B, Hh, D, g))) return st;
-  if (g.padded) return STA_ERR_NOT_TILE_MULTIPLE;
   if (dt != STA_BF16 || !fwd_raster_supported((int)D, g)) return STA_ERR_UNSUPPORTED;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return STA_ERR_ALIGN;

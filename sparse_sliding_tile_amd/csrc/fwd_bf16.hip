@@ -192,9 +192,10 @@ __device__ __forceinline__ uint32_t raster_row(int a0, int a1, int a2, uint32_t 
 
 // MASS: the window mass (v and o unused): K blocks only, no P V; the head
 // table holds the full window and ma the candidate windows (see MassArgs).
-// RASTER: q, k, v, o and lse are in raster order (a latent of whole tiles
-// whose tile width is a multiple of a copy segment's rows): the reorder and
-// unreorder happen in the kernel's own loads and stores.
+// RASTER: q, k, v, o and lse are in raster order (a latent whose tile width
+// is a multiple of a copy segment's rows): the reorder and unreorder happen in
+// the kernel's own loads and stores.  With padding (PADM != 0) the raster
+// tensors hold only the real tokens.
 template <int D, int QT, int NW, int OCC, bool MASS, bool RASTER, int PADM>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -243,7 +244,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 5, c32 = lane & 31;
 
-  const size_t seq = ((size_t)b * Hh + head) * (size_t)g.S;
+  // Rows per (batch, head) sequence: the padded tile-major length, or, for
+  // a raster-order tensor (real tokens only), T*H*W.
+  const size_t seq = ((size_t)b * Hh + head) * (size_t)(RASTER ? g.Sr : g.S);
   const uint16_t* kb = k + seq * D;
   const uint16_t* vb = v + seq * D;
 
@@ -253,20 +256,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // Q^T fragments (B operand): lane holds 8 consecutive d of its query row.
   // qrow[qt]: the lane's query row inside the sequence (tile-major, or its
   // raster position).
+  // A raster-order tensor has no rows for padding positions: their queries
+  // are zeros here and their outputs are not written.
   const int qrow0 = qtile * g.L + sub * C::ROWS + wave * QT * 32;
   uint32_t qrow[QT];
+  bool qreal[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int tm = qrow0 + qt * 32 + c32;
-    qrow[qt] = RASTER ? raster_row(a0, a1, a2, (uint32_t)(tm - qtile * g.L), g) : (uint32_t)tm;
+    qreal[qt] = PADM == 0 || token_real(a0, a1, a2, tm - qtile * g.L, g);
+    qrow[qt] = RASTER ? (qreal[qt] ? raster_row(a0, a1, a2, (uint32_t)(tm - qtile * g.L), g) : 0u)
+                      : (uint32_t)tm;
   }
   bf16x8 qf[QT][C::KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      qf[qt][ks] =
-          as_bf16x8(*(const u32x4*)(q + (seq + qrow[qt]) * D + ks * 16 + grp * 8));
+      qf[qt][ks] = (!RASTER || qreal[qt])
+                       ? as_bf16x8(*(const u32x4*)(q + (seq + qrow[qt]) * D + ks * 16 + grp * 8))
+                       : bf16x8{};
   const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
   const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
             s2 = window_start(a2, w2, g.n2);
@@ -291,7 +300,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // Raster instance: the intra-tile part of the raster row of each copy
   // segment's first row (the same for every key tile), tabulated once; a
   // segment's raster row is then its key tile's origin plus the entry.
+  // With padding, seg_coord holds the segment's intra-tile coordinates
+  // (t, h, first w; 10 bits each) for the copies of partial key tiles.
   __shared__ uint32_t seg_intra[RASTER ? kMaxRasterSegs : 1];
+  __shared__ uint32_t seg_coord[RASTER && PADM != 0 ? kMaxRasterSegs : 1];
   if constexpr (RASTER) {
     constexpr int RPS = KvDma<D, KB, NW>::RPS;
     for (int i = tid; i < g.L / RPS; i += C::THREADS) {
@@ -299,6 +311,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       const uint32_t t0 = fdiv(r, g.fhw), rem = r - t0 * (uint32_t)(g.h * g.w);
       const uint32_t t1 = fdiv(rem, g.fw), t2 = rem - t1 * (uint32_t)g.w;
       seg_intra[i] = (t0 * (uint32_t)g.H + t1) * (uint32_t)g.W + t2;
+      if constexpr (PADM != 0) seg_coord[i] = (t0 << 20) | (t1 << 10) | t2;
     }
     __syncthreads();
   }
@@ -311,13 +324,35 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       using Cp = KvDma<D, KB, NW>;
       const uint32_t org = ((uint32_t)((s0 + i0) * g.t) * (uint32_t)g.H + (uint32_t)((s1 + i1) * g.h)) *
                                (uint32_t)g.W + (uint32_t)((s2 + i2) * g.w);
-      uint32_t rows[Cp::PT];
+      uint32_t rows[Cp::PT], offs[Cp::PT];
 #pragma unroll
-      for (int e = 0; e < Cp::PT; ++e)
-        rows[e] = org + __builtin_amdgcn_readfirstlane(
-                            seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
-      next_key0();
-      copier.issue_rows(kb, vb, rows, kl, vl);
+      for (int e = 0; e < Cp::PT; ++e) {
+        offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
+        rows[e] = org + offs[e];
+      }
+      if constexpr (PADM != 0) {
+        // Copies addressed from the key tile's origin row; in a partial key
+        // tile, the lane's row of each of its segments is real or padding
+        // (the segment's t and h are the same for its rows, w runs along them).
+        uint32_t bits = ~0u;
+        if (tile_partial(s0 + i0, s1 + i1, s2 + i2, g)) {
+          const int e0 = tile_ext(s0 + i0, g.t, g.T), e1 = tile_ext(s1 + i1, g.h, g.H),
+                    e2 = tile_ext(s2 + i2, g.w, g.W);
+          bits = 0;
+#pragma unroll
+          for (int e = 0; e < Cp::PT; ++e) {
+            const uint32_t c = __builtin_amdgcn_readfirstlane(
+                seg_coord[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
+            const bool th = (int)(c >> 20) < e0 && (int)((c >> 10) & 1023u) < e1;
+            bits |= (th && (int)(c & 1023u) + lane / (D / 8) < e2 ? 1u : 0u) << e;
+          }
+        }
+        next_key0();
+        copier.issue_rows_masked(kb, vb, org, offs, bits, lane, kl, vl);
+      } else {
+        next_key0();
+        copier.issue_rows(kb, vb, rows, kl, vl);
+      }
     } else {
       copier.issue(kb, vb, (size_t)next_key0(), kl, vl);
     }
@@ -550,6 +585,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const bool real = PADM == 0 || token_real(a0, a1, a2, rin, g);
     const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow[qt];
+    if (RASTER && !real) continue;  // no raster row for a padding position
     if constexpr (!MASS) {
       // padding rows: a select, not a product (their sums need not be finite)
 #pragma unroll
@@ -600,9 +636,9 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
   const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
-  // Padded latents get instances of their own (the key mask and the zeroed
-  // padding rows); the raster instance takes whole-tile latents only.
-  if constexpr (!RASTER) {
+  // Padded latents get instances of their own (the key mask, the zeroed or
+  // skipped padding rows).
+  {
     if (g.padded) {
       if (g.w == 8 && g.t * g.h <= 64)
         hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 1>), dim3((uint32_t)total),
@@ -656,8 +692,9 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 bool fwd_raster_supported(int D, const Geometry& g) {
   // a copy segment (1 KiB) holds 1024 / (2 D) rows; they must be consecutive
   // raster rows, so the tile width must be a multiple of that count
-  return fwd_bf16_supported(D, g.L) && !g.padded && g.w % (512 / D) == 0 &&
-         g.L / (512 / D) <= kMaxRasterSegs;
+  // (padded latents: the copies' coordinate table packs t, h, w in 10 bits)
+  return fwd_bf16_supported(D, g.L) && g.w % (512 / D) == 0 && g.L / (512 / D) <= kMaxRasterSegs &&
+         (!g.padded || (g.t <= 1024 && g.h <= 1024 && g.w <= 1024));
 }
 
 hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -152,6 +152,75 @@ def test_forward_raster_matches_oracle_and_reorder_path(sta, latent, tile, B, wi
     assert torch.equal(lr.view(torch.int32), lse.view(torch.int32))
 
 
+RASTER_PADDED_CASES = [  # latent, tile, B, windows, D: padded latents in one launch
+    ((5, 15, 13), (2, 4, 4), 2, [(3, 3, 3), (2, 1, 4)], 128),    # -> (6, 16, 16), L = 32, one wave
+    ((11, 30, 29), (2, 8, 8), 1, [(3, 3, 3), (1, 2, 2)], 128),   # -> (12, 32, 32), L = 128, four waves
+    ((3, 14, 29), (1, 8, 8), 1, [(1, 3, 3), (3, 1, 5)], 128),    # -> (3, 16, 32), L = 64, two waves
+    ((5, 16, 20), (1, 8, 8), 1, [(3, 3, 3)], 64),                # D = 64 (8-row copy segments)
+    ((7, 9, 23), (3, 4, 8), 1, [(3, 3, 3), (1, 2, 2)], 128),     # t * h = 12 rows, partial in every dim
+]
+
+
+@pytest.mark.parametrize("latent,tile,B,wins,D", RASTER_PADDED_CASES)
+def test_forward_raster_padded_matches_oracle_and_reorder_path(sta, latent, tile, B, wins, D):
+    """Padded latents on the one-launch raster path: the raster tensors hold
+    only the real tokens; O and LSE are within tolerance of the oracle (padded
+    tile-major, then cropped back to raster) and bit-identical to tile_reorder
+    (zero padding) -> sta_forward -> tile_unreorder."""
+    S = int(np.prod(latent))
+    x = I.make_inputs(B, len(wins), S, D, "bf16", seed=12)
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sta.forward_raster(q, k, v, latent, tile, wins)
+    rq, rk, rv = (O.pad_reorder(to64(x[n]), latent, tile) for n in ("q", "k", "v"))
+    ro, rl = O.forward(rq, rk, rv, latent, tile, wins, D ** -0.5)
+    ro_r = O.pad_unreorder(ro, latent, tile)
+    rl_r = O.pad_unreorder(rl[..., None], latent, tile)[..., 0]
+    eo, el = err_report(to64(o), ro_r), err_report(to64(lse), rl_r)
+    print("O", eo, "LSE", el)
+    assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+    assert el["max_abs"] < BF16_TOL
+    qt, kt, vt = (sta.tile_reorder(a, latent, tile) for a in (q, k, v))
+    ot, lt = sta.forward(qt, kt, vt, latent, tile, wins)
+    assert torch.equal(sta.tile_unreorder(ot, latent, tile).view(torch.int16), o.view(torch.int16))
+    lr = sta.tile_unreorder(lt.unsqueeze(-1), latent, tile).squeeze(-1)
+    assert torch.equal(lr.view(torch.int32), lse.view(torch.int32))
+
+
+def test_forward_raster_padded_29x45x76(sta):
+    """The pages' padding example in one launch: (29,45,76) -> (30,48,80) with
+    tile (6,8,8), 24 heads, window (3,3,3).  Bit-identical to the reorder path
+    over the whole tensor, and sampled raster rows against the oracle."""
+    name = "hunyuan_29x45x76_w333_padded"
+    w = I.WORKLOADS[name]
+    latent, tile, wins, D = w["latent"], w["tile"], w["windows"], w["head_dim"]
+    print(f"[raster padded] {name}", flush=True)
+    x = I.workload_inputs(name)
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sta.forward_raster(q, k, v, latent, tile, wins)
+    qt, kt, vt = (sta.tile_reorder(a, latent, tile) for a in (q, k, v))
+    ot, lt = sta.forward(qt, kt, vt, latent, tile, wins)
+    assert torch.equal(sta.tile_unreorder(ot, latent, tile).view(torch.int16), o.view(torch.int16))
+    lr = sta.tile_unreorder(lt.unsqueeze(-1), latent, tile).squeeze(-1)
+    assert torch.equal(lr.view(torch.int32), lse.view(torch.int32))
+    del qt, kt, vt, ot, lt
+    # sampled raster rows: the oracle's tile-major rows of those tokens
+    T, H, W = latent
+    grid = O.padded_latent(latent, tile)
+    pi = O.tile_major_index(grid, tile)
+    rng = np.random.default_rng(3)
+    rr = np.unique(np.concatenate([[0, T * H * W - 1, (T - 1) * H * W, H * W - 1], rng.integers(0, T * H * W, 60)]))
+    tau, y, xx = rr // (H * W), (rr // W) % H, rr % W
+    tm_rows = pi[(tau * grid[1] + y) * grid[2] + xx]
+    rt = torch.from_numpy(rr).cuda()
+    for h in (0, 23):
+        hq, hk, hv = (O.pad_reorder(to64(x[nm][:, h:h + 1]), latent, tile) for nm in ("q", "k", "v"))
+        ro, rl = O.forward(hq, hk, hv, latent, tile, [wins[h]], D ** -0.5, rows=tm_rows)
+        eo, el = err_report(to64(o[:, h:h + 1, rt]), ro), err_report(to64(lse[:, h:h + 1, rt]), rl)
+        print("head", h, "O", eo, "LSE", el)
+        assert eo["max_abs"] < BF16_TOL and eo["rel_rms"] < BF16_REL_RMS
+        assert el["max_abs"] < BF16_TOL
+
+
 def test_forward_raster_hunyuan_bit_identical(sta):
     """(30,48,80), tile (6,8,8), 24 heads, mixed windows: the raster instance
     equals reorder -> sta_forward -> unreorder bit for bit."""
