@@ -280,12 +280,32 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
             s2 = window_start(a2, w2, g.n2);
   const int bpt = g.L / KB;
-  const int nblk = w0 * w1 * w2 * bpt;
+  // Key blocks walked per key tile.  In a padded latent a key tile ends at the
+  // block that holds its last real (t, h) row (tile-major order inside the
+  // tile): the blocks after it hold padding keys only, whose scores would all
+  // be masked to -inf and add exactly nothing, so they are neither copied nor
+  // computed.  (Padding along w alone never empties a block whose rows are
+  // real.)  Only the last tile along an axis is partial, so a tile's count
+  // depends on whether it is the last along t and along h, and the walks
+  // work it out when their w index wraps.
+  const int x0 = tile_ext(g.n0 - 1, g.t, g.T), x1 = tile_ext(g.n1 - 1, g.h, g.H);
+  auto blocks_th = [&](int e0, int e1) -> int { return (((e0 - 1) * g.h + e1) * g.w + KB - 1) / KB; };
+  auto tile_blocks = [&](int k0, int k1) -> int {
+    if constexpr (PADM == 0) return bpt;
+    return blocks_th(k0 == g.n0 - 1 ? x0 : g.t, k1 == g.n1 - 1 ? x1 : g.h);
+  };
+  int nblk = w0 * w1 * w2 * bpt;
+  if constexpr (PADM != 0) {
+    const int l0 = s0 + w0 == g.n0, l1 = s1 + w1 == g.n1;
+    nblk = w2 * ((w0 - l0) * ((w1 - l1) * bpt + l1 * blocks_th(g.t, x1)) +
+                 l0 * ((w1 - l1) * blocks_th(x0, g.h) + l1 * blocks_th(x0, x1)));
+  }
 
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;  // key-block walk, incremented
+  int kbt = tile_blocks(s0, s1);        // blocks of the walk's key tile
   auto next_key0 = [&]() -> int {
     const int key0 = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L + jb * KB;
-    if (++jb == bpt) {
+    if (++jb == kbt) {
       jb = 0;
       if (++i2 == w2) {
         i2 = 0;
@@ -293,6 +313,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
           i1 = 0;
           ++i0;
         }
+        if constexpr (PADM != 0) kbt = tile_blocks(s0 + i0, s1 + i1);
       }
     }
     return key0;
@@ -300,18 +321,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // Raster instance: the intra-tile part of the raster row of each copy
   // segment's first row (the same for every key tile), tabulated once; a
   // segment's raster row is then its key tile's origin plus the entry.
-  // With padding, seg_coord holds the segment's intra-tile coordinates
-  // (t, h, first w; 10 bits each) for the copies of partial key tiles.
-  __shared__ uint32_t seg_intra[RASTER ? kMaxRasterSegs : 1];
-  __shared__ uint32_t seg_coord[RASTER && PADM != 0 ? kMaxRasterSegs : 1];
+  // With padding, seg_tab pairs that entry with the segment's intra-tile
+  // coordinates (t, h, first w; 10 bits each) for the copies of partial key
+  // tiles, one 64-bit entry so that a stage waits for a single LDS read.
+  __shared__ uint32_t seg_intra[RASTER && PADM == 0 ? kMaxRasterSegs : 1];
+  __shared__ uint2 seg_tab[RASTER && PADM != 0 ? kMaxRasterSegs : 1];
   if constexpr (RASTER) {
     constexpr int RPS = KvDma<D, KB, NW>::RPS;
     for (int i = tid; i < g.L / RPS; i += C::THREADS) {
       const uint32_t r = (uint32_t)(i * RPS);
       const uint32_t t0 = fdiv(r, g.fhw), rem = r - t0 * (uint32_t)(g.h * g.w);
       const uint32_t t1 = fdiv(rem, g.fw), t2 = rem - t1 * (uint32_t)g.w;
-      seg_intra[i] = (t0 * (uint32_t)g.H + t1) * (uint32_t)g.W + t2;
-      if constexpr (PADM != 0) seg_coord[i] = (t0 << 20) | (t1 << 10) | t2;
+      const uint32_t intra = (t0 * (uint32_t)g.H + t1) * (uint32_t)g.W + t2;
+      if constexpr (PADM != 0)
+        seg_tab[i] = make_uint2(intra, (t0 << 20) | (t1 << 10) | t2);
+      else
+        seg_intra[i] = intra;
     }
     __syncthreads();
   }
@@ -325,31 +350,31 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       const uint32_t org = ((uint32_t)((s0 + i0) * g.t) * (uint32_t)g.H + (uint32_t)((s1 + i1) * g.h)) *
                                (uint32_t)g.W + (uint32_t)((s2 + i2) * g.w);
       uint32_t rows[Cp::PT], offs[Cp::PT];
-#pragma unroll
-      for (int e = 0; e < Cp::PT; ++e) {
-        offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
-        rows[e] = org + offs[e];
-      }
       if constexpr (PADM != 0) {
-        // Copies addressed from the key tile's origin row; in a partial key
-        // tile, the lane's row of each of its segments is real or padding
-        // (the segment's t and h are the same for its rows, w runs along them).
-        uint32_t bits = ~0u;
-        if (tile_partial(s0 + i0, s1 + i1, s2 + i2, g)) {
-          const int e0 = tile_ext(s0 + i0, g.t, g.T), e1 = tile_ext(s1 + i1, g.h, g.H),
-                    e2 = tile_ext(s2 + i2, g.w, g.W);
-          bits = 0;
+        // Copies addressed from the key tile's origin row.  The lane's row of
+        // each of its segments is real when its coordinates lie inside the
+        // key tile's real extent (a segment's t and h are the same for its
+        // rows, w runs along them); in a whole tile every row passes, so the
+        // test needs no branch on the tile.
+        const int e0 = tile_ext(s0 + i0, g.t, g.T), e1 = tile_ext(s1 + i1, g.h, g.H),
+                  e2 = tile_ext(s2 + i2, g.w, g.W);
+        uint32_t bits = 0;
 #pragma unroll
-          for (int e = 0; e < Cp::PT; ++e) {
-            const uint32_t c = __builtin_amdgcn_readfirstlane(
-                seg_coord[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
-            const bool th = (int)(c >> 20) < e0 && (int)((c >> 10) & 1023u) < e1;
-            bits |= (th && (int)(c & 1023u) + lane / (D / 8) < e2 ? 1u : 0u) << e;
-          }
+        for (int e = 0; e < Cp::PT; ++e) {
+          const uint2 sc = seg_tab[jb * (KB / Cp::RPS) + copier.wave_u + e * NW];
+          offs[e] = __builtin_amdgcn_readfirstlane(sc.x);
+          const uint32_t c = __builtin_amdgcn_readfirstlane(sc.y);
+          const bool th = (int)(c >> 20) < e0 && (int)((c >> 10) & 1023u) < e1;
+          bits |= (th && (int)(c & 1023u) + lane / (D / 8) < e2 ? 1u : 0u) << e;
         }
         next_key0();
         copier.issue_rows_masked(kb, vb, org, offs, bits, lane, kl, vl);
       } else {
+#pragma unroll
+        for (int e = 0; e < Cp::PT; ++e) {
+          offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
+          rows[e] = org + offs[e];
+        }
         next_key0();
         copier.issue_rows(kb, vb, rows, kl, vl);
       }
@@ -362,7 +387,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // out of the stage being computed (a second walk over the key blocks).  The
   // mass instance also reads off the walk whether the stage ends its key tile
   // and which candidate windows hold that tile.
-  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
+  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0, ckbt = tile_blocks(s0, s1);
   bool tile_done = false;
   uint32_t member = 0;
   // Mass instance: the start of every candidate window of this query tile
@@ -406,7 +431,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       }
     }
     if constexpr (MASS) {
-      tile_done = cjb == bpt - 1;
+      tile_done = cjb == ckbt - 1;
       if (cjb == 0) {  // a new key tile: which candidate windows hold it
         member = 0;
 #pragma unroll
@@ -455,7 +480,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
             if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
       }
     }
-    if (++cjb == bpt) {
+    if (++cjb == ckbt) {
       cjb = 0;
       if (++ci2 == w2) {
         ci2 = 0;
@@ -463,6 +488,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
           ci1 = 0;
           ++ci0;
         }
+        if constexpr (PADM != 0) ckbt = tile_blocks(s0 + ci0, s1 + ci1);
       }
     }
   };
@@ -554,7 +580,34 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
     pv_stage<D, QT>(vf, pf, oacc);
   };
-  if constexpr (SLOTS == 4) {
+  // A wave whose query rows are all padding (a padded latent) computes
+  // nothing: it waits, joins every barrier and issues its share of the
+  // copies like the others, and its outputs are the padding rows' zeros.
+  bool any_real = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) any_real |= qreal[qt];
+  if (PADM != 0 && __ballot(any_real) == 0) {
+    auto idle = [&](int j, char* kl_far, char* vl_far) {
+      if (j + 1 < nblk) {
+        wait_next(j);
+        barrier_lds();
+        if (j + AHEAD < nblk) issue(kl_far, vl_far);
+      }
+    };
+    if constexpr (SLOTS == 4) {
+      for (int j = 0; j < nblk; j += 4) {
+        idle(j, kl3, vl3);
+        idle(j + 1, kl0, vl0);
+        idle(j + 2, kl1, vl1);
+        idle(j + 3, kl2, vl2);
+      }
+    } else {
+      for (int j = 0; j < nblk; j += 2) {
+        idle(j, kl0, vl0);
+        idle(j + 1, kl1, vl1);
+      }
+    }
+  } else if constexpr (SLOTS == 4) {
     // stage j reads slot (j + 1) % 4 and refills slot (j + 3) % 4
     for (int j = 0; j < nblk; j += 4) {
       stage(j, vfa, vfb, kl1, vl1, kl3, vl3);
