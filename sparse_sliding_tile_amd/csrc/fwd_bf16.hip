@@ -85,23 +85,26 @@ __device__ __forceinline__ float xmax32_raw(float x) {
 }
 
 // Online softmax of one stage (lazy rescale), producing the bf16 P^T operand.
+// mlim = mrun + the rescale threshold, kept beside mrun so that a stage
+// compares without an add.
 template <int D, int QT>
 __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (&pf)[QT][2],
                                               f32x16 (&oacc)[QT][D / 32], float (&mrun)[QT],
-                                              float (&lrun)[QT], float c_log2) {
+                                              float (&mlim)[QT], float (&lrun)[QT], float c_log2) {
   bool need = false;
   float mblk[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     mblk[qt] = xmax32_raw(block_max16(sacc[qt])) * c_log2;
-    need |= mblk[qt] > mrun[qt] + kRescaleThreshold;
+    need |= mblk[qt] > mlim[qt];
   }
   if (__any(need)) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float mn = fmaxf(mrun[qt], mblk[qt]);
+      const float mn = vmax2(mrun[qt], mblk[qt]);  // finite block maxima: no NaN to order
       const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mn);
       mrun[qt] = mn;
+      mlim[qt] = mn + kRescaleThreshold;
       lrun[qt] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
@@ -117,15 +120,15 @@ __device__ __forceinline__ void softmax_stage(const f32x16 (&sacc)[QT], bf16x8 (
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         pf[qt][s][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][8 * s + e], c_log2, mneg));
-    // Row sum of the bf16 probabilities (the values P V uses), two per dot2.
+    // Row sum of the bf16 probabilities (the values P V uses), two per dot2,
+    // accumulated straight into the running sum.
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[qt][0][2 * e], pf[qt][0][2 * e + 1]}, one, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[qt][1][2 * e], pf[qt][1][2 * e + 1]}, one, ls1, false);
-    }
-    lrun[qt] += ls0 + ls1;
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        lrun[qt] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[qt][s][2 * e], pf[qt][s][2 * e + 1]}, one,
+                                                   lrun[qt], false);
   }
 }
 
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       using Cp = KvDma<D, KB, NW>;
       const uint32_t org = ((uint32_t)((s0 + i0) * g.t) * (uint32_t)g.H + (uint32_t)((s1 + i1) * g.h)) *
                                (uint32_t)g.W + (uint32_t)((s2 + i2) * g.w);
-      uint32_t rows[Cp::PT], offs[Cp::PT];
+      uint32_t offs[Cp::PT];
       if constexpr (PADM != 0) {
         // Copies addressed from the key tile's origin row.  The lane's row of
         // each of its segments is real when its coordinates lie inside the
@@ -370,13 +373,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         next_key0();
         copier.issue_rows_masked(kb, vb, org, offs, bits, lane, kl, vl);
       } else {
+        // (every row real: the same origin-based copies, a scalar base and a
+        // 32-bit lane offset per segment)
 #pragma unroll
-        for (int e = 0; e < Cp::PT; ++e) {
+        for (int e = 0; e < Cp::PT; ++e)
           offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
-          rows[e] = org + offs[e];
-        }
         next_key0();
-        copier.issue_rows(kb, vb, rows, kl, vl);
+        copier.issue_rows_masked(kb, vb, org, offs, ~0u, lane, kl, vl);
       }
     } else {
       copier.issue(kb, vb, (size_t)next_key0(), kl, vl);
@@ -494,13 +497,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   };
 
   f32x16 oacc[QT][C::DT];
-  float mrun[QT], lrun[QT];
+  float mrun[QT], mlim[QT], lrun[QT];
   float ltile[QT], lcand[QT][kMaxCandidates];  // mass instance only
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] = f32x16{};
     mrun[qt] = -INFINITY;
+    mlim[qt] = -INFINITY;
     lrun[qt] = 0.f;
     ltile[qt] = 0.f;
 #pragma unroll
@@ -568,7 +572,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     // SIMD compete for issue, the one in its softmax goes first and the
     // other's matrix instructions fill the gaps (measured +2%).
     __builtin_amdgcn_s_setprio(2);
-    softmax_stage<D, QT>(sacc, pf, oacc, mrun, lrun, c_log2);
+    softmax_stage<D, QT>(sacc, pf, oacc, mrun, mlim, lrun, c_log2);
     __builtin_amdgcn_s_setprio(0);
     if (j + 1 < nblk) {
       wait_next(j);
