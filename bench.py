@@ -351,7 +351,8 @@ def main():
         legs["tile_unreorder"] = {"ms": round(u_ms, 4), "GB/s": round(nbytes / u_ms / 1e6, 1),
                                   "frac_of_hbm_peak": round(nbytes / u_ms / 1e6 / PEAK_HBM_GBS, 3),
                                   "tensor": list(q.shape)}
-        del x, q, k, v, qt, kt, vt, ot, o, lse
+        # (q, k, v, o, lse stay: the padded raster leg alternates with the bench step)
+        del x, qt, kt, vt, ot
         torch.cuda.empty_cache()
         g = torch.Generator(device=dev).manual_seed(1)
 
@@ -428,7 +429,9 @@ def main():
                     with wtm:
                         sta.forward_raster(q, k, v, latent, tile, wins, out=o, lse=lse)
                 torch.cuda.synchronize()
-                rms, wms = rtm.total_ms() / 10, wtm.total_ms() / 10
+                # medians of the per-call times: one slow stretch of the run
+                # does not move them
+                rms, wms = rtm.each_ms()[5], wtm.each_ms()[5]
                 legs[lname + "_raster_step"] = {
                     "ms": round(rms, 3), "tflops": round(lf / rms / 1e9, 1),
                     "pct_of_peak": round(100 * lf / rms / 1e9 / PEAK_BF16_TFLOPS, 2),
@@ -436,9 +439,10 @@ def main():
                     "whole_tile_step_ms_alternated": round(wms, 3),
                     "over_whole_tile_step": round(rms / wms, 4),
                     "over_timed_bench_step": round(rms / ms_step, 4),
-                    "note": "sta_forward_raster, one launch, raster tensors of the real tokens; "
-                            "over_whole_tile_step = this time / the (30,48,80) bench step timed in "
-                            "alternation with it"}
+                    "ms_mean": round(rtm.total_ms() / 10, 3),
+                    "note": "sta_forward_raster, one launch, raster tensors of the real tokens; median of "
+                            "10 calls; over_whole_tile_step = this time / the (30,48,80) bench step timed "
+                            "in alternation with it (median of 10)"}
                 del ra, rb, rc, rout, rl
             if lname.endswith("mixed"):
                 legs[lname]["windows"] = [list(x_) for x_ in lw["windows"]]

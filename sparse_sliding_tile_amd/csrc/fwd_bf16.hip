@@ -354,24 +354,34 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
                                (uint32_t)g.W + (uint32_t)((s2 + i2) * g.w);
       uint32_t offs[Cp::PT];
       if constexpr (PADM != 0) {
-        // Copies addressed from the key tile's origin row.  The lane's row of
-        // each of its segments is real when its coordinates lie inside the
-        // key tile's real extent (a segment's t and h are the same for its
-        // rows, w runs along them); in a whole tile every row passes, so the
-        // test needs no branch on the tile.
+        // Copies addressed from the key tile's origin row.  In a partial key
+        // tile the lane's row of each of its segments is real when its
+        // coordinates lie inside the tile's real extent (a segment's t and h
+        // are the same for its rows, w runs along them); whole tiles (most
+        // stages) skip the test.
         const int e0 = tile_ext(s0 + i0, g.t, g.T), e1 = tile_ext(s1 + i1, g.h, g.H),
                   e2 = tile_ext(s2 + i2, g.w, g.W);
-        uint32_t bits = 0;
+        const bool partial = e0 < g.t || e1 < g.h || e2 < g.w;
+        uint32_t coord[Cp::PT];
 #pragma unroll
         for (int e = 0; e < Cp::PT; ++e) {
           const uint2 sc = seg_tab[jb * (KB / Cp::RPS) + copier.wave_u + e * NW];
           offs[e] = __builtin_amdgcn_readfirstlane(sc.x);
-          const uint32_t c = __builtin_amdgcn_readfirstlane(sc.y);
-          const bool th = (int)(c >> 20) < e0 && (int)((c >> 10) & 1023u) < e1;
-          bits |= (th && (int)(c & 1023u) + lane / (D / 8) < e2 ? 1u : 0u) << e;
+          coord[e] = __builtin_amdgcn_readfirstlane(sc.y);
         }
         next_key0();
-        copier.issue_rows_masked(kb, vb, org, offs, bits, lane, kl, vl);
+        if (partial) {
+          bool real[Cp::PT];
+#pragma unroll
+          for (int e = 0; e < Cp::PT; ++e) {
+            const uint32_t c = coord[e];
+            real[e] = (int)(c >> 20) < e0 && (int)((c >> 10) & 1023u) < e1 &&
+                      (int)(c & 1023u) + lane / (D / 8) < e2;
+          }
+          copier.issue_rows_masked(kb, vb, org, offs, real, lane, kl, vl);
+        } else {
+          copier.issue_rows_origin(kb, vb, org, offs, kl, vl);
+        }
       } else {
         // (every row real: the same origin-based copies, a scalar base and a
         // 32-bit lane offset per segment)
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         for (int e = 0; e < Cp::PT; ++e)
           offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
         next_key0();
-        copier.issue_rows_masked(kb, vb, org, offs, ~0u, lane, kl, vl);
+        copier.issue_rows_origin(kb, vb, org, offs, kl, vl);
       }
     } else {
       copier.issue(kb, vb, (size_t)next_key0(), kl, vl);

@@ -209,16 +209,31 @@ struct KvDma {
       dma16((const char*)(vg + (size_t)seg_row[e] * D) + in_seg, vl + seg * 1024);
     }
   }
-  // The same gather for a key tile that holds padding (a latent that is not a
-  // whole number of tiles), addressed from the key tile's origin row
-  // (origin_row, scalar): seg_off[e] is the raster offset of segment e's
-  // first row from that origin (scalar, never negative).  Lanes whose row is
-  // padding (bit e of real_bits clear) copy 16 bytes of the origin row itself,
-  // a real row, so every staged value is finite and no read leaves the tensor;
-  // the attention masks those keys.
+  // The same gather addressed from a key tile's origin row (origin_row,
+  // scalar): seg_off[e] is the raster offset of segment e's first row from
+  // that origin (scalar, never negative).  One scalar base per tensor and a
+  // 32-bit lane offset per segment.
+  __device__ __forceinline__ void issue_rows_origin(const uint16_t* kg, const uint16_t* vg,
+                                                    uint32_t origin_row, const uint32_t (&seg_off)[PT],
+                                                    char* kl, char* vl) const {
+    const char* kbase = (const char*)(kg + (size_t)origin_row * D);
+    const char* vbase = (const char*)(vg + (size_t)origin_row * D);
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+      const int seg = wave_u + e * NW;
+      const uint32_t in_seg = goff[e] - (uint32_t)(seg * RPS * D * 2);
+      const uint32_t off = seg_off[e] * (uint32_t)(D * 2) + in_seg;
+      dma16(kbase + off, kl + seg * 1024);
+      dma16(vbase + off, vl + seg * 1024);
+    }
+  }
+  // The same for a key tile that holds padding (a latent that is not a whole
+  // number of tiles): lanes whose row is padding (real[e] false) copy 16
+  // bytes of the origin row itself, a real row, so every staged value is
+  // finite and no read leaves the tensor; the attention masks those keys.
   __device__ __forceinline__ void issue_rows_masked(const uint16_t* kg, const uint16_t* vg,
                                                     uint32_t origin_row, const uint32_t (&seg_off)[PT],
-                                                    uint32_t real_bits, int lane, char* kl,
+                                                    const bool (&real)[PT], int lane, char* kl,
                                                     char* vl) const {
     constexpr int CPR = D / 8;  // chunks per row
     const char* kbase = (const char*)(kg + (size_t)origin_row * D);
@@ -228,7 +243,7 @@ struct KvDma {
     for (int e = 0; e < PT; ++e) {
       const int seg = wave_u + e * NW;
       const uint32_t in_seg = goff[e] - (uint32_t)(seg * RPS * D * 2);
-      const uint32_t off = ((real_bits >> e) & 1u) ? seg_off[e] * (uint32_t)(D * 2) + in_seg : pad_off;
+      const uint32_t off = real[e] ? seg_off[e] * (uint32_t)(D * 2) + in_seg : pad_off;
       dma16(kbase + off, kl + seg * 1024);
       dma16(vbase + off, vl + seg * 1024);
     }
