@@ -231,6 +231,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   const int spt = g.L / kStage;
   const int nst = w0 * w1 * w2 * spt;
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;
+  // lane offsets of the K/V copies worked out once (scalar base per issue)
+  const KvDma<D, kStage, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
   auto issue = [&](char* kl, char* vl) {
     const int key0 = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L + jb * kStage;
     if (++jb == spt) {
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
         }
       }
     }
-    dma_kv<D, kStage, NW>(kb, vb, (size_t)key0, kl, vl, wave, lane);
+    copier.issue(kb, vb, (size_t)key0, kl, vl);
   };
 
   f32x16 acc[DT];
@@ -464,6 +466,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   const int spt = g.L / kStage;
   const int nst = c0 * c1 * c2 * spt;
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;
+  // lane offsets of the Q/dO copies worked out once (scalar base per issue)
+  const KvDma<D, kStage, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
   auto issue = [&](char* ql, char* dol, char* st) {
     const size_t q0 =
         (size_t)(((lo0 + i0) * g.n1 + (lo1 + i1)) * g.n2 + (lo2 + i2)) * g.L + jb * kStage;
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
         }
       }
     }
-    dma_kv<D, kStage, NW>(qb, db, q0, ql, dol, wave, lane);
+    copier.issue(qb, db, q0, ql, dol);
     dma_stats<D>(lse2, dl, seq + q0, st, wave, lane);
   };
 
