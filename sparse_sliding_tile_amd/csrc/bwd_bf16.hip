@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(q + row * D + ks * 16 + grp * 8));
   // The wave's 32 dO rows go to its LDS tile (the staged tiles' swizzle) and
-  // are read back as the dP^T B operand each stage.
+  // are read from there once into the registers of the dP^T B operand.
   char* dotile = dores + wave * TB;
   {
     constexpr int RPS = 1024 / (D * 2), CPR = D / 8;
@@ -317,20 +317,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     }
   };
 
+  bf16x8 dof[KS];  // the wave's dO rows (B operand of dP^T), read once from its tile
   auto step = [&](const char* kl, const char* vl) {
     bf16x8 kf[KS], vr[KS];
     read_rows<D>(kl, kf, grp, c32);
     read_rows<D>(vl, vr, grp, c32);
     f32x16 st = contract_rows<D>(kf, qf);         // S^T[key][q]
-    // a scheduling boundary after S^T (the dP^T reads stay below it:
-    // measured faster)
+    // a scheduling boundary after S^T (measured faster)
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 dpt;
-    {
-      bf16x8 dof[KS];
-      read_rows<D>(dotile, dof, grp, c32);
-      dpt = contract_rows<D>(vr, dof);              // dP^T[key][q]
-    }
+    const f32x16 dpt = contract_rows<D>(vr, dof);  // dP^T[key][q]
     f32x16 dsf;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -358,6 +353,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   issue(kl0, vl0);
   if (nst > 1) issue(kl1, vl1);
   wait_stage<PER>(nst > 1 ? 1 : 0);   // the dO tile and stage 0 have landed
+  read_rows<D>(dotile, dof, grp, c32);  // the wave's own tile: no barrier needed
   barrier_lds();
   // Both slots in one loop body with no exit in between (an exit there made
   // the compiler copy the accumulators every other stage); an odd last stage
@@ -439,13 +435,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 
   // Resident key rows: K^T as the B operand (lane holds 8 d of key c32); for
   // dK the wave's 32 V rows are copied into its LDS tile (swizzled like the
-  // staged tiles) and read back per stage.
+  // staged tiles) and read from there once into registers (vrow).
   const size_t krow0 = seq + (size_t)ktile * g.L + sub * (NW * 32) + wave * 32;
   bf16x8 kf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     kf[ks] = as_bf16x8(*(const u32x4*)(k + (krow0 + c32) * D + ks * 16 + grp * 8));
   char* vtile = vres + (MODE == 1 ? wave * TB : 0);
+  bf16x8 vrow[MODE == 1 ? KS : 1];
   if constexpr (MODE == 1) {
     constexpr int RPS = 1024 / (D * 2), CPR = D / 8;
     const int rin = lane / CPR, p = lane % CPR;
@@ -567,9 +564,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
     }
     if constexpr (MODE == 1) {
-      bf16x8 da[KS], vf[KS];
+      bf16x8 da[KS];
       read_rows<D>(dol, da, grp, c32);
-      read_rows<D>(vtile, vf, grp, c32);
       // dP - Dl: the accumulation starts from -Dl of the element's query
       // (stage statistics, already in the accumulator's layout)
       f32x16 ndl;
@@ -579,7 +575,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) ndl[4 * i + jj] = d4[jj];
       }
-      dp = contract_rows_from<D>(da, vf, ndl);  // dP[q][key] - Dl[q]
+      dp = contract_rows_from<D>(da, vrow, ndl);  // dP[q][key] - Dl[q]
     }
     // lane's queries: 8i + 4g + jj; the A operand is P^T (MODE 0) or dS^T.
     float pe[16];
@@ -623,6 +619,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   // odd last stage runs after it.
   issue(ql0, dol0, st0);
   wait_dma();
+  if constexpr (MODE == 1) read_rows<D>(vtile, vrow, grp, c32);  // the wave's own tile
   barrier_lds();
   int j = 0;
   for (; j + 1 < nst; j += 2) {
