@@ -181,6 +181,15 @@ struct KvDma {
       goff[e] = (uint32_t)(r * D + ((p ^ (int)swz<D>(r)) * 8)) * 2u;
     }
   }
+  // Lane offset e, opaque to the optimiser at each use: otherwise it hoists
+  // the loop-invariant sum of tensor base and lane offset into a 64-bit
+  // register pair and adds each block's row offset with 64-bit vector adds,
+  // where the scalar-base form needs none.
+  __device__ __forceinline__ uint32_t lane_off(int e) const {
+    uint32_t o = goff[e];
+    asm volatile("" : "+v"(o));
+    return o;
+  }
   // Rows [row0, row0 + ROWS) of kg and vg into the tiles kl and vl.
   __device__ __forceinline__ void issue(const uint16_t* kg, const uint16_t* vg, size_t row0, char* kl,
                                         char* vl) const {
@@ -189,8 +198,9 @@ struct KvDma {
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
       const int seg = wave_u + e * NW;
-      dma16(kbase + goff[e], kl + seg * 1024);
-      dma16(vbase + goff[e], vl + seg * 1024);
+      const uint32_t o = lane_off(e);
+      dma16(kbase + o, kl + seg * 1024);
+      dma16(vbase + o, vl + seg * 1024);
     }
   }
   // The same block gathered from a raster-order sequence: seg_row[e] is the
@@ -252,7 +262,7 @@ struct KvDma {
   __device__ __forceinline__ void issue_k(const uint16_t* kg, size_t row0, char* kl) const {
     const char* kbase = (const char*)(kg + row0 * D);
 #pragma unroll
-    for (int e = 0; e < PT; ++e) dma16(kbase + goff[e], kl + (wave_u + e * NW) * 1024);
+    for (int e = 0; e < PT; ++e) dma16(kbase + lane_off(e), kl + (wave_u + e * NW) * 1024);
   }
 };
 
