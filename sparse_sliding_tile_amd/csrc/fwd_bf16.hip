@@ -306,6 +306,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
 
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;  // key-block walk, incremented
   int kbt = tile_blocks(s0, s1);        // blocks of the walk's key tile
+  // Raster instance: the walk's key tile as its raster origin row and, with
+  // padding, its real extent per axis; worked out when the walk reaches the
+  // tile, not per block.
+  uint32_t korg = 0;
+  int ke0 = g.t, ke1 = g.h, ke2 = g.w;
+  bool kpart = false;
+  auto enter_tile = [&]() {
+    if constexpr (RASTER) {
+      const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
+      korg = ((uint32_t)(k0 * g.t) * (uint32_t)g.H + (uint32_t)(k1 * g.h)) * (uint32_t)g.W +
+             (uint32_t)(k2 * g.w);
+      if constexpr (PADM != 0) {
+        ke0 = tile_ext(k0, g.t, g.T);
+        ke1 = tile_ext(k1, g.h, g.H);
+        ke2 = tile_ext(k2, g.w, g.W);
+        kpart = ke0 < g.t || ke1 < g.h || ke2 < g.w;
+      }
+    }
+  };
+  enter_tile();
   auto next_key0 = [&]() -> int {
     const int key0 = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L + jb * KB;
     if (++jb == kbt) {
@@ -318,6 +338,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         }
         if constexpr (PADM != 0) kbt = tile_blocks(s0 + i0, s1 + i1);
       }
+      enter_tile();
     }
     return key0;
   };
@@ -350,8 +371,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     } else if constexpr (RASTER) {
       // raster rows of this block's segments (scalar: the same in every lane)
       using Cp = KvDma<D, KB, NW>;
-      const uint32_t org = ((uint32_t)((s0 + i0) * g.t) * (uint32_t)g.H + (uint32_t)((s1 + i1) * g.h)) *
-                               (uint32_t)g.W + (uint32_t)((s2 + i2) * g.w);
+      const uint32_t org = korg;
       uint32_t offs[Cp::PT];
       if constexpr (PADM != 0) {
         // Copies addressed from the key tile's origin row.  In a partial key
@@ -359,9 +379,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         // coordinates lie inside the tile's real extent (a segment's t and h
         // are the same for its rows, w runs along them); whole tiles (most
         // stages) skip the test.
-        const int e0 = tile_ext(s0 + i0, g.t, g.T), e1 = tile_ext(s1 + i1, g.h, g.H),
-                  e2 = tile_ext(s2 + i2, g.w, g.W);
-        const bool partial = e0 < g.t || e1 < g.h || e2 < g.w;
+        const int e0 = ke0, e1 = ke1, e2 = ke2;
+        const bool partial = kpart;
         uint32_t coord[Cp::PT];
 #pragma unroll
         for (int e = 0; e < Cp::PT; ++e) {
