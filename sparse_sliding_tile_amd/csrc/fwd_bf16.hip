@@ -306,15 +306,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
 
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;  // key-block walk, incremented
   int kbt = tile_blocks(s0, s1);        // blocks of the walk's key tile
-  // Raster instance: the walk's key tile as its raster origin row and, with
-  // padding, its real extent per axis; worked out when the walk reaches the
-  // tile, not per block.
+  // The walk's key tile as its first tile-major row (korg) or, in the raster
+  // instance, its raster origin row and, with padding, its real extent per
+  // axis; worked out when the walk reaches the tile, not per block.
   uint32_t korg = 0;
   int ke0 = g.t, ke1 = g.h, ke2 = g.w;
   bool kpart = false;
   auto enter_tile = [&]() {
-    if constexpr (RASTER) {
-      const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
+    const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
+    if constexpr (!RASTER) {
+      korg = (uint32_t)(((k0 * g.n1 + k1) * g.n2 + k2) * g.L);
+    } else {
       korg = ((uint32_t)(k0 * g.t) * (uint32_t)g.H + (uint32_t)(k1 * g.h)) * (uint32_t)g.W +
              (uint32_t)(k2 * g.w);
       if constexpr (PADM != 0) {
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   };
   enter_tile();
   auto next_key0 = [&]() -> int {
-    const int key0 = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L + jb * KB;
+    const int key0 = RASTER ? 0 : (int)korg + jb * KB;  // (the raster copies use korg)
     if (++jb == kbt) {
       jb = 0;
       if (++i2 == w2) {
