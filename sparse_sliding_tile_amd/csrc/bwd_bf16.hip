@@ -233,8 +233,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;
   // lane offsets of the K/V copies worked out once (scalar base per issue)
   const KvDma<D, kStage, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
+  // first row of the walk's key tile, worked out when the walk enters it
+  int ktrow = ((s0 * g.n1 + s1) * g.n2 + s2) * g.L;
   auto issue = [&](char* kl, char* vl) {
-    const int key0 = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L + jb * kStage;
+    const int key0 = ktrow + jb * kStage;
     if (++jb == spt) {
       jb = 0;
       if (++i2 == w2) {
@@ -244,6 +246,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
           ++i0;
         }
       }
+      ktrow = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L;
     }
     copier.issue(kb, vb, (size_t)key0, kl, vl);
   };
@@ -465,9 +468,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;
   // lane offsets of the Q/dO copies worked out once (scalar base per issue)
   const KvDma<D, kStage, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
+  // first row of the walk's query tile, worked out when the walk enters it
+  int qtrow = ((lo0 * g.n1 + lo1) * g.n2 + lo2) * g.L;
   auto issue = [&](char* ql, char* dol, char* st) {
-    const size_t q0 =
-        (size_t)(((lo0 + i0) * g.n1 + (lo1 + i1)) * g.n2 + (lo2 + i2)) * g.L + jb * kStage;
+    const size_t q0 = (size_t)(qtrow + jb * kStage);
     if (++jb == spt) {
       jb = 0;
       if (++i2 == c2) {
@@ -477,6 +481,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
           ++i0;
         }
       }
+      qtrow = (((lo0 + i0) * g.n1 + (lo1 + i1)) * g.n2 + (lo2 + i2)) * g.L;
     }
     copier.issue(qb, db, q0, ql, dol);
     dma_stats<D>(lse2, dl, seq + q0, st, wave, lane);
