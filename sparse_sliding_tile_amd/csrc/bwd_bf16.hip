@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   // Two-stage LDS ring: stage j sits in slot j % 2; its copy is issued two
   // stages ahead, right after the barrier that ends stage j - 2 (every wave
   // has then finished reading that slot: each step consumes its reads).
-  constexpr int PER = dma_kv_per_wave<D, kStage, NW>();
+  constexpr int PER = KvDma<D, kStage, NW>::PER;  // copies per wave per stage
   issue(kl0, vl0);
   if (nst > 1) issue(kl1, vl1);
   wait_stage<PER>(nst > 1 ? 1 : 0);   // the dO tile and stage 0 have landed

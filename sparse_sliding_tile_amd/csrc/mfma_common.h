@@ -93,13 +93,6 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
-// DMA instructions one wave issues for one dma_kv call (uniform over waves
-// when the segment count splits evenly).
-template <int D, int ROWS, int NW>
-constexpr int dma_kv_per_wave() {
-  return (2 * (ROWS / (1024 / (D * 2)))) / NW;
-}
-
 // Padding mask of one 32-row block: bit r is set when intra-tile position
 // row0 + r of tile (a0, a1, a2) holds a real token.  The same value in every
 // lane (a ballot; every lane must call it).
@@ -121,48 +114,18 @@ __device__ __forceinline__ bool elem_real(uint32_t bits, int e) {
 }
 
 // x combined with the value of lane l ^ 32 (v_permlane32_swap).
-__device__ __forceinline__ float xmax32(float x) {
-  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
 __device__ __forceinline__ float xsum32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Copies the K and V blocks [ROWS x D] (ROWS consecutive sequence rows from
-// grow) into LDS in the swizzled layout with 16-byte DMA.  The 1 KiB segments
-// of both tiles are dealt round-robin over the NW waves of the workgroup.
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_kv(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-                                       size_t grow, char* kl, char* vl, int wave, int lane) {
-  constexpr int RPS = 1024 / (D * 2);       // rows per 1 KiB segment
-  constexpr int SEGS = ROWS / RPS;          // segments per tile
-  static_assert(ROWS % RPS == 0, "block rows must fill whole segments");
-  constexpr int CPR = D / 8;                // chunks per row
-  constexpr int PER = (2 * SEGS + NW - 1) / NW;
-  static_assert(PER < 64, "too many copies per wave");
-  const int rin = lane / CPR;
-  const int p = lane % CPR;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int seg2 = wave + e * NW;
-    if ((2 * SEGS) % NW == 0 || seg2 < 2 * SEGS) {
-      const bool isv = seg2 >= SEGS;
-      const int seg = isv ? seg2 - SEGS : seg2;
-      const int r = seg * RPS + rin;
-      const int c = p ^ (int)swz<D>(r);
-      dma16((isv ? vg : kg) + (grow + r) * D + c * 8, (isv ? vl : kl) + seg * 1024);
-    }
-  }
-}
-
-// The same copy with the per-lane parts worked out once: the source offset of
-// each lane's 16 bytes inside a block and the wave's LDS segments do not change
-// from block to block, so an issue costs one scalar base address per tensor
-// (the loads use the scalar-base + 32-bit lane-offset addressing form).  The
-// segments of each tile are dealt round-robin over the NW waves; wave_u must be
-// the wave index held uniformly (readfirstlane).
+// Copies of K and V blocks [ROWS x D] into LDS tiles in the swizzled layout
+// with 16-byte DMA.  The 1 KiB segments of each tile are dealt round-robin
+// over the NW waves of the workgroup; the source offset of each lane's 16
+// bytes inside a block and the wave's LDS segments do not change from block
+// to block, so they are worked out once and an issue costs one scalar base per
+// tensor (the loads use the scalar-base + 32-bit lane-offset addressing form).
+// wave_u must be the wave index held uniformly (readfirstlane).
 template <int D, int ROWS, int NW>
 struct KvDma {
   static constexpr int RPS = 1024 / (D * 2);  // rows per 1 KiB segment
@@ -203,26 +166,11 @@ struct KvDma {
       dma16(vbase + o, vl + seg * 1024);
     }
   }
-  // The same block gathered from a raster-order sequence: seg_row[e] is the
-  // raster row of the first of the RPS rows of segment wave + e * NW (those
-  // rows must be consecutive in raster order).
-  __device__ __forceinline__ void issue_rows(const uint16_t* kg, const uint16_t* vg,
-                                             const uint32_t (&seg_row)[PT], char* kl,
-                                             char* vl) const {
-#pragma unroll
-    for (int e = 0; e < PT; ++e) {
-      const int seg = wave_u + e * NW;
-      // goff[e] counts from the block's first row; the lane's offset inside
-      // its segment drops the segment's first seg * RPS rows.
-      const uint32_t in_seg = goff[e] - (uint32_t)(seg * RPS * D * 2);
-      dma16((const char*)(kg + (size_t)seg_row[e] * D) + in_seg, kl + seg * 1024);
-      dma16((const char*)(vg + (size_t)seg_row[e] * D) + in_seg, vl + seg * 1024);
-    }
-  }
-  // The same gather addressed from a key tile's origin row (origin_row,
-  // scalar): seg_off[e] is the raster offset of segment e's first row from
-  // that origin (scalar, never negative).  One scalar base per tensor and a
-  // 32-bit lane offset per segment.
+  // The same block gathered from a raster-order sequence, addressed from a
+  // key tile's origin row (origin_row, scalar): seg_off[e] is the raster
+  // offset of the first of the RPS rows of segment wave + e * NW from that
+  // origin (scalar, never negative; those rows must be consecutive in raster
+  // order).  One scalar base per tensor and a 32-bit lane offset per segment.
   __device__ __forceinline__ void issue_rows_origin(const uint16_t* kg, const uint16_t* vg,
                                                     uint32_t origin_row, const uint32_t (&seg_off)[PT],
                                                     char* kl, char* vl) const {
