@@ -42,7 +42,9 @@ the pages are silent:
     keys, and the rows of padding tokens are outputs of no real token (O, LSE
     and all gradients are zero there).
 Every function here is pinned by ``tests/test_oracle.py`` against brute force,
-closed forms, invariants and library routines.
+closed forms, invariants and library routines.  One case is parity unpinned by
+the pages: an even window narrower than the tile grid, where the pages do not
+say on which side the extra tile falls; the tests pin only the reading above.
 """
 
 import numpy as np
