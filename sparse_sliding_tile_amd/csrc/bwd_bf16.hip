@@ -223,6 +223,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     }
   }
   const float lrow = lse2[row], ndrow = dl[row];  // -Dl
+  // -Dl in every element: each stage's dP^T accumulation starts from this
+  // block (the lane's query, hence its Dl, is the same for the whole walk),
+  // so dS = P (dP - Dl) takes no subtraction.
+  f32x16 ndl16;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ndl16[e] = ndrow;
 
   const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
   const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
@@ -328,12 +334,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     f32x16 st = contract_rows<D>(kf, qf);         // S^T[key][q]
     // a scheduling boundary after S^T (measured faster)
     __builtin_amdgcn_sched_barrier(0);
-    const f32x16 dpt = contract_rows<D>(vr, dof);  // dP^T[key][q]
+    const f32x16 dpt = contract_rows_from<D>(vr, dof, ndl16);  // dP^T[key][q] - Dl[q]
     f32x16 dsf;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(fmaf(st[e], c_log2, -lrow));
-      dsf[e] = p * (dpt[e] + ndrow);
+      dsf[e] = p * dpt[e];
     }
     mask_keys(dsf);
     bf16x8 ds[2];
