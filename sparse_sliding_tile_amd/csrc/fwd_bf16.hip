@@ -304,14 +304,29 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
                  l0 * ((w1 - l1) * blocks_th(x0, g.h) + l1 * blocks_th(x0, x1)));
   }
 
+  // Mass instance: the start of every candidate window of this query tile
+  // (fixed for the whole walk).
+  int cs[MASS ? kMaxCandidates : 1][3];
+  if constexpr (MASS) {
+#pragma unroll
+    for (int c = 0; c < kMaxCandidates; ++c) {
+      const bool use = c < ma.ncand;
+      cs[c][0] = use ? window_start(a0, ma.w[c][0], g.n0) : 0;
+      cs[c][1] = use ? window_start(a1, ma.w[c][1], g.n1) : 0;
+      cs[c][2] = use ? window_start(a2, ma.w[c][2], g.n2) : 0;
+    }
+  }
+
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;  // key-block walk, incremented
   int kbt = tile_blocks(s0, s1);        // blocks of the walk's key tile
-  // The walk's key tile as its first tile-major row (korg) or, in the raster
-  // instance, its raster origin row and, with padding, its real extent per
-  // axis; worked out when the walk reaches the tile, not per block.
+  // The walk's key tile, worked out when the walk reaches it, not per block:
+  // its first tile-major row (korg) or, in the raster instance, its raster
+  // origin row and, with padding, its real extent per axis; in the mass
+  // instance the candidate windows that hold it (kmember, one bit each).
   uint32_t korg = 0;
   int ke0 = g.t, ke1 = g.h, ke2 = g.w;
   bool kpart = false;
+  uint32_t kmember = 0;
   auto enter_tile = [&]() {
     const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
     if constexpr (!RASTER) {
@@ -324,6 +339,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         ke1 = tile_ext(k1, g.h, g.H);
         ke2 = tile_ext(k2, g.w, g.W);
         kpart = ke0 < g.t || ke1 < g.h || ke2 < g.w;
+      }
+    }
+    if constexpr (MASS) {
+      kmember = 0;
+#pragma unroll
+      for (int c = 0; c < kMaxCandidates; ++c) {
+        if (c < ma.ncand) {
+          const bool in = (unsigned)(k0 - cs[c][0]) < (unsigned)ma.w[c][0] &&
+                          (unsigned)(k1 - cs[c][1]) < (unsigned)ma.w[c][1] &&
+                          (unsigned)(k2 - cs[c][2]) < (unsigned)ma.w[c][2];
+          kmember |= (in ? 1u : 0u) << c;
+        }
       }
     }
   };
@@ -367,7 +394,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     __syncthreads();
   }
   const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
-  auto issue = [&](char* kl, char* vl) {
+  // Mass instance: what the stage computing a block needs beyond its keys,
+  // worked out when the block's copy is issued and kept beside its ring slot
+  // (the loops are unrolled by the slot count, so each slot's copy is a fixed
+  // register): bits 0-7 the candidate windows holding the block's key tile,
+  // bit 31 set when the block is its tile's last.
+  struct BlockInfo {
+    uint32_t mass;
+  };
+  auto issue = [&](char* kl, char* vl, BlockInfo& bi) {
+    if constexpr (MASS) bi.mass = kmember | (jb == kbt - 1 ? 0x80000000u : 0u);
     if constexpr (MASS) {
       copier.issue_k(kb, (size_t)next_key0(), kl);
     } else if constexpr (RASTER) {
@@ -417,27 +453,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
   };
 
-  // Padded latents: keys at padding positions of a partial key tile are masked
-  // out of the stage being computed (a second walk over the key blocks).  The
-  // mass instance also reads off the walk whether the stage ends its key tile
-  // and which candidate windows hold that tile.
-  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0, ckbt = tile_blocks(s0, s1);
-  bool tile_done = false;
-  uint32_t member = 0;
-  // Mass instance: the start of every candidate window of this query tile
-  // (fixed for the whole walk).
-  int cs[MASS ? kMaxCandidates : 1][3];
-  if constexpr (MASS) {
-#pragma unroll
-    for (int c = 0; c < kMaxCandidates; ++c) {
-      const bool use = c < ma.ncand;
-      cs[c][0] = use ? window_start(a0, ma.w[c][0], g.n0) : 0;
-      cs[c][1] = use ? window_start(a1, ma.w[c][1], g.n1) : 0;
-      cs[c][2] = use ? window_start(a2, ma.w[c][2], g.n2) : 0;
-    }
-  }
   // Padding masks (PADM, one instance each): 0 whole-tile latent, no mask;
-  // 1 tiles 8 keys wide with at most 64 tile rows; 2 any other tile.
+  // 1 tiles 8 keys wide with at most 64 tile rows; 2 any other tile.  Keys at
+  // padding positions of a partial key tile are masked out of the stage being
+  // computed, found by a second walk over the key blocks (in step with the
+  // stages, a few scalar instructions each, which the matrix products hide).
   // PADM 1: a 32-key block is 4 tile rows of 8, and element e of lane l in
   // the S^T accumulator holds row e / 4 of the block and column 4 (l / 32) +
   // e % 4 of the tile.  A key is real when its row (i0, i1) and its column
@@ -446,83 +466,69 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // columns to -inf (a select, so any finite padding contents, even ones whose
   // products overflow, are masked exactly).
   // PADM 2 tests every key of the block (ballot per stage).
-  constexpr bool row_col_mask = PADM == 1;
+  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0, ckbt = tile_blocks(s0, s1);
   bool key_tile_partial = false, col_partial = false;
   uint64_t rows_real = ~0ull;  // bit R: tile row R is real
   int col_ext = 8;             // real columns of the key tile
   auto mask_keys = [&](f32x16 (&sacc)[QT]) {
-    if (!MASS && PADM == 0) return;
-    const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
-    if (row_col_mask && cjb == 0) {  // a new key tile
-      key_tile_partial = tile_partial(k0, k1, k2, g);
-      if (key_tile_partial) {
-        const int e0 = tile_ext(k0, g.t, g.T), e1 = tile_ext(k1, g.h, g.H), e2 = tile_ext(k2, g.w, g.W);
-        const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
-        const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
-        rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
-        col_ext = e2;
-        col_partial = e2 < 8;
-      }
-    }
-    if constexpr (MASS) {
-      tile_done = cjb == ckbt - 1;
-      if (cjb == 0) {  // a new key tile: which candidate windows hold it
-        member = 0;
-#pragma unroll
-        for (int c = 0; c < kMaxCandidates; ++c) {
-          if (c < ma.ncand) {
-            const bool in = (unsigned)(k0 - cs[c][0]) < (unsigned)ma.w[c][0] &&
-                            (unsigned)(k1 - cs[c][1]) < (unsigned)ma.w[c][1] &&
-                            (unsigned)(k2 - cs[c][2]) < (unsigned)ma.w[c][2];
-            member |= (in ? 1u : 0u) << c;
+    if constexpr (PADM != 0) {
+      const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
+      if constexpr (PADM == 1) {
+        if (cjb == 0) {  // a new key tile
+          key_tile_partial = tile_partial(k0, k1, k2, g);
+          if (key_tile_partial) {
+            const int e0 = tile_ext(k0, g.t, g.T), e1 = tile_ext(k1, g.h, g.H), e2 = tile_ext(k2, g.w, g.W);
+            const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
+            const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
+            rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
+            col_ext = e2;
+            col_partial = e2 < 8;
           }
         }
-      }
-    }
-    if constexpr (row_col_mask) {
-      if (key_tile_partial) {
-        const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
-        if (rb != 0xfu) {  // a row of the block is padding (uniform)
+        if (key_tile_partial) {
+          const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
+          if (rb != 0xfu) {  // a row of the block is padding (uniform)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool rreal = (rb >> u) & 1u;
+            for (int u = 0; u < 4; ++u) {
+              const bool rreal = (rb >> u) & 1u;
+#pragma unroll
+              for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                  sacc[qt][4 * u + jj] = rreal ? sacc[qt][4 * u + jj] : -INFINITY;
+            }
+          }
+          if (col_partial) {
+            bool creal[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj)
-                sacc[qt][4 * u + jj] = rreal ? sacc[qt][4 * u + jj] : -INFINITY;
+              for (int e = 0; e < 16; ++e) sacc[qt][e] = creal[e & 3] ? sacc[qt][e] : -INFINITY;
           }
         }
-        if (col_partial) {
-          bool creal[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
+      } else if (tile_partial(k0, k1, k2, g)) {
+        const uint32_t m = block_real_mask(k0, k1, k2, cjb * KB, g, lane);
+        if (m != 0xffffffffu) {  // blocks of a partial tile are often whole
+          const uint32_t bits = lane_bits(m, lane);
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[qt][e] = creal[e & 3] ? sacc[qt][e] : -INFINITY;
+            for (int e = 0; e < 16; ++e)
+              if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
         }
       }
-    } else if (PADM == 2 && tile_partial(k0, k1, k2, g)) {
-      const uint32_t m = block_real_mask(k0, k1, k2, cjb * KB, g, lane);
-      if (m != 0xffffffffu) {  // blocks of a partial tile are often whole
-        const uint32_t bits = lane_bits(m, lane);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
-      }
-    }
-    if (++cjb == ckbt) {
-      cjb = 0;
-      if (++ci2 == w2) {
-        ci2 = 0;
-        if (++ci1 == w1) {
-          ci1 = 0;
-          ++ci0;
+      if (++cjb == ckbt) {
+        cjb = 0;
+        if (++ci2 == w2) {
+          ci2 = 0;
+          if (++ci1 == w1) {
+            ci1 = 0;
+            ++ci0;
+          }
+          ckbt = tile_blocks(s0 + ci0, s1 + ci1);
         }
-        if constexpr (PADM != 0) ckbt = tile_blocks(s0 + ci0, s1 + ci1);
       }
     }
   };
@@ -556,10 +562,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   constexpr int SLOTS = NW >= 4 ? 4 : 2;
   constexpr int AHEAD = SLOTS == 4 ? 3 : 2;
   constexpr int PER = MASS ? KvDma<D, KB, NW>::PT : KvDma<D, KB, NW>::PER;
-  issue(kl0, vl0);
-  if (nblk > 1) issue(kl1, vl1);
+  BlockInfo bi0{}, bi1{}, bi2{}, bi3{};  // ring slots 0..3
+  issue(kl0, vl0, bi0);
+  if (nblk > 1) issue(kl1, vl1, bi1);
   if constexpr (SLOTS == 4) {
-    if (nblk > 2) issue(kl2, vl2);
+    if (nblk > 2) issue(kl2, vl2, bi2);
     if (nblk > 2) wait_dma_upto<2 * PER>();
     else wait_dma();
   } else {
@@ -582,19 +589,25 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   read_rows<D>(kl0, kf, grp, c32);
   if constexpr (!MASS) read_cols<D>(vl0, vfa, lane);
 
+  // bi_cur describes stage j's block, bi_far receives the block copied into
+  // the slot being refilled (the same slot with two slots: bi_cur is read
+  // before the copy is issued).
   auto stage = [&](int j, bf16x8 (&vf)[C::DT][2], bf16x8 (&vf_nxt)[C::DT][2], const char* kl_nxt,
-                   const char* vl_nxt, char* kl_far, char* vl_far) {
+                   const char* vl_nxt, char* kl_far, char* vl_far, const BlockInfo& bi_cur,
+                   BlockInfo& bi_far) {
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
     mask_keys(sacc);
     if constexpr (MASS) {
+      const bool tile_done = (bi_cur.mass >> 31) != 0u;
+      const uint32_t member = bi_cur.mass & 0xffu;
       mass_stage<QT>(sacc, mrun, lrun, ltile, lcand, ma.ncand, tile_done, member, c_log2);
       if (j + 1 < nblk) {
         wait_next(j);
         barrier_lds();
         read_rows<D>(kl_nxt, kf, grp, c32);
         asm volatile("" ::: "memory");
-        if (j + AHEAD < nblk) issue(kl_far, vl_far);
+        if (j + AHEAD < nblk) issue(kl_far, vl_far, bi_far);
       }
       return;
     }
@@ -611,7 +624,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       read_rows<D>(kl_nxt, kf, grp, c32);
       read_cols<D>(vl_nxt, vf_nxt, lane);
       asm volatile("" ::: "memory");
-      if (j + AHEAD < nblk) issue(kl_far, vl_far);
+      if (j + AHEAD < nblk) issue(kl_far, vl_far, bi_far);
     }
     pv_stage<D, QT>(vf, pf, oacc);
   };
@@ -622,11 +635,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) any_real |= qreal[qt];
   if (PADM != 0 && __ballot(any_real) == 0) {
+    BlockInfo unused{};
     auto idle = [&](int j, char* kl_far, char* vl_far) {
       if (j + 1 < nblk) {
         wait_next(j);
         barrier_lds();
-        if (j + AHEAD < nblk) issue(kl_far, vl_far);
+        if (j + AHEAD < nblk) issue(kl_far, vl_far, unused);
       }
     };
     if constexpr (SLOTS == 4) {
@@ -645,21 +659,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   } else if constexpr (SLOTS == 4) {
     // stage j reads slot (j + 1) % 4 and refills slot (j + 3) % 4
     for (int j = 0; j < nblk; j += 4) {
-      stage(j, vfa, vfb, kl1, vl1, kl3, vl3);
+      stage(j, vfa, vfb, kl1, vl1, kl3, vl3, bi0, bi3);
       if (j + 1 >= nblk) break;
-      stage(j + 1, vfb, vfa, kl2, vl2, kl0, vl0);
+      stage(j + 1, vfb, vfa, kl2, vl2, kl0, vl0, bi1, bi0);
       if (j + 2 >= nblk) break;
-      stage(j + 2, vfa, vfb, kl3, vl3, kl1, vl1);
+      stage(j + 2, vfa, vfb, kl3, vl3, kl1, vl1, bi2, bi1);
       if (j + 3 >= nblk) break;
-      stage(j + 3, vfb, vfa, kl0, vl0, kl2, vl2);
+      stage(j + 3, vfb, vfa, kl0, vl0, kl2, vl2, bi3, bi2);
     }
   } else {
     // stage j reads slot (j + 1) % 2 and refills slot j % 2 (read by every
     // wave one stage earlier)
     for (int j = 0; j < nblk; j += 2) {
-      stage(j, vfa, vfb, kl1, vl1, kl0, vl0);
+      stage(j, vfa, vfb, kl1, vl1, kl0, vl0, bi0, bi0);
       if (j + 1 >= nblk) break;
-      stage(j + 1, vfb, vfa, kl0, vl0, kl1, vl1);
+      stage(j + 1, vfb, vfa, kl0, vl0, kl1, vl1, bi1, bi1);
     }
   }
 
