@@ -130,8 +130,9 @@ int sta_tile_pairs_host(int32_t* pairs_host, int64_t* head_offsets_host, sta_dim
  *   tile lies in the window of a,   LSE_i = ln sum_j exp(scale * <q_i, k_j>).
  * q, k, v, o: [B, Hh, S', D] in TILE-MAJOR order (see sta_tile_reorder).
  * lse: fp32 [B, Hh, S'] or NULL.  scale > 0 (usually 1/sqrt(D)).
- * STA_BF16: bf16 in/out, fp32 accumulation, MFMA; needs D in {64, 128} and
- * L % 32 == 0.  STA_F32: fp32 in/out, fp32 arithmetic; needs D in {32, 64, 128}. */
+ * STA_BF16: bf16 in/out, fp32 accumulation, MFMA; needs D in {64, 128},
+ * L % 32 == 0 and, for a latent that is not a whole number of tiles,
+ * L <= 2^20.  STA_F32: fp32 in/out, fp32 arithmetic; needs D in {32, 64, 128}. */
 int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                 int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile, const int32_t* win_host,
                 float scale, sta_dtype dt, void* stream);
@@ -148,9 +149,8 @@ int sta_forward(const void* q, const void* k, const void* v, void* o, float* lse
  * only the T*H*W real tokens (padding positions have no rows, are never
  * keys and produce no output).  Needs STA_BF16 with D in {64, 128},
  * L % 32 == 0, the tile width a multiple of 512 / D and
- * L <= 1024 * 512 / D, i.e. 4096 tokens for D = 128 and 8192 for D = 64,
- * and for a padded latent tile sides t, h, w <= 1024 (STA_ERR_UNSUPPORTED
- * otherwise).  Other arguments as sta_forward. */
+ * L <= 1024 * 512 / D, i.e. 4096 tokens for D = 128 and 8192 for D = 64
+ * (STA_ERR_UNSUPPORTED otherwise).  Other arguments as sta_forward. */
 int sta_forward_raster(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t Hh, int64_t D, sta_dim3 latent, sta_dim3 tile,
                        const int32_t* win_host, float scale, sta_dtype dt, void* stream);

@@ -185,7 +185,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, fl
     return STA_ERR_ALIGN;
   const hipStream_t s = (hipStream_t)stream;
   if (dt == STA_BF16) {
-    if (!fwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
+    if (!fwd_bf16_supported((int)D, g)) return STA_ERR_UNSUPPORTED;
     return to_status(launch_fwd_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                      (uint16_t*)o, lse, g, ht, (int)B, (int)Hh, (int)D, scale, s));
   }
@@ -389,7 +389,7 @@ int sta_window_mass(const void* q, const void* k, float* mass, void* workspace, 
   if ((st = check_sizes(B, Hh, D, g))) return st;
   if (Hh > STA_MAX_HEADS || n_cand > STA_MAX_CANDIDATES) return STA_ERR_UNSUPPORTED;
   if (dt == STA_BF16) {
-    if (!fwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
+    if (!fwd_bf16_supported((int)D, g)) return STA_ERR_UNSUPPORTED;
   } else if (dt == STA_F32) {
     if (D != 32 && D != 64 && D != 128) return STA_ERR_UNSUPPORTED;
   } else {

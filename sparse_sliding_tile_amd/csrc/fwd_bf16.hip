@@ -283,25 +283,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
             s2 = window_start(a2, w2, g.n2);
   const int bpt = g.L / KB;
-  // Key blocks walked per key tile.  In a padded latent a key tile ends at the
-  // block that holds its last real (t, h) row (tile-major order inside the
-  // tile): the blocks after it hold padding keys only, whose scores would all
-  // be masked to -inf and add exactly nothing, so they are neither copied nor
-  // computed.  (Padding along w alone never empties a block whose rows are
-  // real.)  Only the last tile along an axis is partial, so a tile's count
-  // depends on whether it is the last along t and along h, and the walks
-  // work it out when their w index wraps.
-  const int x0 = tile_ext(g.n0 - 1, g.t, g.T), x1 = tile_ext(g.n1 - 1, g.h, g.H);
-  auto blocks_th = [&](int e0, int e1) -> int { return (((e0 - 1) * g.h + e1) * g.w + KB - 1) / KB; };
-  auto tile_blocks = [&](int k0, int k1) -> int {
-    if constexpr (PADM == 0) return bpt;
-    return blocks_th(k0 == g.n0 - 1 ? x0 : g.t, k1 == g.n1 - 1 ? x1 : g.h);
-  };
+  // Padded latents (PADM 1): the real keys of a partial key tile are walked
+  // compacted, in the tile's own (t, h, w) order with the padding positions
+  // left out, so the tile takes ceil(real keys / 32) blocks and only the last
+  // of them can hold padding, at its end.  Whole tiles are walked as they
+  // are (L / 32 blocks).  Only the last tile along an axis is partial, so the
+  // window's block count is a sum over the 8 classes (last along t, h, w or
+  // not) of the class's tile count times its blocks.
+  auto tile_blocks = [&](int e0, int e1, int e2) -> int { return (e0 * e1 * e2 + KB - 1) / KB; };
   int nblk = w0 * w1 * w2 * bpt;
   if constexpr (PADM != 0) {
-    const int l0 = s0 + w0 == g.n0, l1 = s1 + w1 == g.n1;
-    nblk = w2 * ((w0 - l0) * ((w1 - l1) * bpt + l1 * blocks_th(g.t, x1)) +
-                 l0 * ((w1 - l1) * blocks_th(x0, g.h) + l1 * blocks_th(x0, x1)));
+    const int x0 = tile_ext(g.n0 - 1, g.t, g.T), x1 = tile_ext(g.n1 - 1, g.h, g.H),
+              x2 = tile_ext(g.n2 - 1, g.w, g.W);
+    const int l0 = s0 + w0 == g.n0, l1 = s1 + w1 == g.n1, l2 = s2 + w2 == g.n2;
+    nblk = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int c0 = c & 1, c1 = (c >> 1) & 1, c2 = c >> 2;
+      const int cnt = (c0 ? l0 : w0 - l0) * (c1 ? l1 : w1 - l1) * (c2 ? l2 : w2 - l2);
+      nblk += cnt * tile_blocks(c0 ? x0 : g.t, c1 ? x1 : g.h, c2 ? x2 : g.w);
+    }
   }
 
   // Mass instance: the start of every candidate window of this query tile
@@ -318,27 +319,35 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   }
 
   int i0 = 0, i1 = 0, i2 = 0, jb = 0;  // key-block walk, incremented
-  int kbt = tile_blocks(s0, s1);        // blocks of the walk's key tile
+  int kbt = bpt;                        // blocks of the walk's key tile
   // The walk's key tile, worked out when the walk reaches it, not per block:
-  // its first tile-major row (korg) or, in the raster instance, its raster
-  // origin row and, with padding, its real extent per axis; in the mass
+  // its first row (korg: tile-major, or the raster row of its origin); with
+  // padding its real extent per axis, its real key count (knreal) and, for a
+  // partial tile, the reciprocals of its real extent along h and w (the
+  // compacted key index is split into (t, h, w) with them); in the mass
   // instance the candidate windows that hold it (kmember, one bit each).
   uint32_t korg = 0;
-  int ke0 = g.t, ke1 = g.h, ke2 = g.w;
+  int ke1 = g.h, ke2 = g.w, knreal = g.L;
   bool kpart = false;
+  float kinv1 = 1.0f, kinv2 = 1.0f;
   uint32_t kmember = 0;
-  auto enter_tile = [&]() {
+  auto enter_tile = [&]() __attribute__((always_inline)) {
     const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
-    if constexpr (!RASTER) {
+    if constexpr (!RASTER)
       korg = (uint32_t)(((k0 * g.n1 + k1) * g.n2 + k2) * g.L);
-    } else {
+    else
       korg = ((uint32_t)(k0 * g.t) * (uint32_t)g.H + (uint32_t)(k1 * g.h)) * (uint32_t)g.W +
              (uint32_t)(k2 * g.w);
-      if constexpr (PADM != 0) {
-        ke0 = tile_ext(k0, g.t, g.T);
-        ke1 = tile_ext(k1, g.h, g.H);
-        ke2 = tile_ext(k2, g.w, g.W);
-        kpart = ke0 < g.t || ke1 < g.h || ke2 < g.w;
+    if constexpr (PADM != 0) {
+      const int e0 = tile_ext(k0, g.t, g.T);
+      ke1 = tile_ext(k1, g.h, g.H);
+      ke2 = tile_ext(k2, g.w, g.W);
+      knreal = e0 * ke1 * ke2;
+      kpart = knreal < g.L;
+      kbt = tile_blocks(e0, ke1, ke2);
+      if (kpart) {  // (scalar registers: the same in every lane)
+        kinv1 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_amdgcn_rcpf((float)ke1))));
+        kinv2 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_amdgcn_rcpf((float)ke2))));
       }
     }
     if constexpr (MASS) {
@@ -355,8 +364,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
   };
   enter_tile();
-  auto next_key0 = [&]() -> int {
-    const int key0 = RASTER ? 0 : (int)korg + jb * KB;  // (the raster copies use korg)
+  auto next_block = [&]() __attribute__((always_inline)) {
     if (++jb == kbt) {
       jb = 0;
       if (++i2 == w2) {
@@ -365,169 +373,102 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
           i1 = 0;
           ++i0;
         }
-        if constexpr (PADM != 0) kbt = tile_blocks(s0 + i0, s1 + i1);
       }
       enter_tile();
     }
-    return key0;
   };
   // Raster instance: the intra-tile part of the raster row of each copy
-  // segment's first row (the same for every key tile), tabulated once; a
-  // segment's raster row is then its key tile's origin plus the entry.
-  // With padding, seg_tab pairs that entry with the segment's intra-tile
-  // coordinates (t, h, first w; 10 bits each) for the copies of partial key
-  // tiles, one 64-bit entry so that a stage waits for a single LDS read.
-  __shared__ uint32_t seg_intra[RASTER && PADM == 0 ? kMaxRasterSegs : 1];
-  __shared__ uint2 seg_tab[RASTER && PADM != 0 ? kMaxRasterSegs : 1];
+  // segment's first row (the same for every whole key tile), tabulated once;
+  // a segment's raster row is then its key tile's origin plus the entry.
+  __shared__ uint32_t seg_intra[RASTER ? kMaxRasterSegs : 1];
   if constexpr (RASTER) {
     constexpr int RPS = KvDma<D, KB, NW>::RPS;
     for (int i = tid; i < g.L / RPS; i += C::THREADS) {
       const uint32_t r = (uint32_t)(i * RPS);
       const uint32_t t0 = fdiv(r, g.fhw), rem = r - t0 * (uint32_t)(g.h * g.w);
       const uint32_t t1 = fdiv(rem, g.fw), t2 = rem - t1 * (uint32_t)g.w;
-      const uint32_t intra = (t0 * (uint32_t)g.H + t1) * (uint32_t)g.W + t2;
-      if constexpr (PADM != 0)
-        seg_tab[i] = make_uint2(intra, (t0 << 20) | (t1 << 10) | t2);
-      else
-        seg_intra[i] = intra;
+      seg_intra[i] = (t0 * (uint32_t)g.H + t1) * (uint32_t)g.W + t2;
     }
     __syncthreads();
   }
-  const KvDma<D, KB, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
-  // Mass instance: what the stage computing a block needs beyond its keys,
-  // worked out when the block's copy is issued and kept beside its ring slot
-  // (the loops are unrolled by the slot count, so each slot's copy is a fixed
-  // register): bits 0-7 the candidate windows holding the block's key tile,
-  // bit 31 set when the block is its tile's last.
+  using Cp = KvDma<D, KB, NW>;
+  const Cp copier(__builtin_amdgcn_readfirstlane(wave), lane);
+  // What the stage computing a block needs beyond its keys, worked out when
+  // the block's copy is issued and kept beside its ring slot (the loops are
+  // unrolled by the slot count, so each slot's copy is a fixed register):
+  //   nvalid: padded latents, the real keys of a block that ends a partial
+  //           key tile with padding (1..31); 0 for a block of real keys only;
+  //   mass:   bits 0-7 the candidate windows holding the block's key tile,
+  //           bit 31 set when the block is its tile's last.
   struct BlockInfo {
+    uint32_t nvalid;
     uint32_t mass;
   };
-  auto issue = [&](char* kl, char* vl, BlockInfo& bi) {
+  // A partial key tile's block: the lane's key of each of its copy segments
+  // is compacted key c = jb * 32 + row, at (c / (e1 e2), (c / e2) % e1,
+  // c % e2) inside the tile (e = the real extents).  The quotients are taken
+  // in fp32 with the reciprocal: c < 2^20, so (c + 0.5) / e lies at least
+  // 2^-21 (relative) away from any integer, beyond the reciprocal's error.
+  auto issue = [&](char* kl, char* vl, BlockInfo& bi) __attribute__((always_inline)) {
+    if constexpr (PADM != 0) bi.nvalid = jb == kbt - 1 ? (uint32_t)(knreal - jb * KB) & (KB - 1) : 0u;
     if constexpr (MASS) bi.mass = kmember | (jb == kbt - 1 ? 0x80000000u : 0u);
-    if constexpr (MASS) {
-      copier.issue_k(kb, (size_t)next_key0(), kl);
-    } else if constexpr (RASTER) {
-      // raster rows of this block's segments (scalar: the same in every lane)
-      using Cp = KvDma<D, KB, NW>;
-      const uint32_t org = korg;
-      uint32_t offs[Cp::PT];
-      if constexpr (PADM != 0) {
-        // Copies addressed from the key tile's origin row.  In a partial key
-        // tile the lane's row of each of its segments is real when its
-        // coordinates lie inside the tile's real extent (a segment's t and h
-        // are the same for its rows, w runs along them); whole tiles (most
-        // stages) skip the test.
-        const int e0 = ke0, e1 = ke1, e2 = ke2;
-        const bool partial = kpart;
-        uint32_t coord[Cp::PT];
+    const uint32_t org = korg;
+    if (PADM != 0 && kpart) {
+      const uint32_t sa = RASTER ? (uint32_t)(g.H * g.W) : (uint32_t)(g.h * g.w);
+      const uint32_t sb = RASTER ? (uint32_t)g.W : (uint32_t)g.w;
+      uint32_t rel[Cp::PT];
+      bool real[Cp::PT];
 #pragma unroll
-        for (int e = 0; e < Cp::PT; ++e) {
-          const uint2 sc = seg_tab[jb * (KB / Cp::RPS) + copier.wave_u + e * NW];
-          offs[e] = __builtin_amdgcn_readfirstlane(sc.x);
-          coord[e] = __builtin_amdgcn_readfirstlane(sc.y);
-        }
-        next_key0();
-        if (partial) {
-          bool real[Cp::PT];
-#pragma unroll
-          for (int e = 0; e < Cp::PT; ++e) {
-            const uint32_t c = coord[e];
-            real[e] = (int)(c >> 20) < e0 && (int)((c >> 10) & 1023u) < e1 &&
-                      (int)(c & 1023u) + lane / (D / 8) < e2;
-          }
-          copier.issue_rows_masked(kb, vb, org, offs, real, lane, kl, vl);
-        } else {
-          copier.issue_rows_origin(kb, vb, org, offs, kl, vl);
-        }
-      } else {
-        // (every row real: the same origin-based copies, a scalar base and a
-        // 32-bit lane offset per segment)
-#pragma unroll
-        for (int e = 0; e < Cp::PT; ++e)
-          offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
-        next_key0();
-        copier.issue_rows_origin(kb, vb, org, offs, kl, vl);
+      for (int e = 0; e < Cp::PT; ++e) {
+        const uint32_t c = (uint32_t)(jb * KB) + copier.row_in_block(e, lane);
+        const uint32_t tr = (uint32_t)(((float)c + 0.5f) * kinv2);  // tile row (t, h)
+        const uint32_t cw = c - tr * (uint32_t)ke2;
+        const uint32_t ct = (uint32_t)(((float)tr + 0.5f) * kinv1);
+        const uint32_t ch = tr - ct * (uint32_t)ke1;
+        real[e] = c < (uint32_t)knreal;
+        rel[e] = ct * sa + ch * sb + cw;
       }
+      next_block();
+      if constexpr (MASS)
+        copier.issue_k_gather(kb, org, rel, real, kl);
+      else
+        copier.issue_rows_gather(kb, vb, org, rel, real, kl, vl);
+    } else if constexpr (RASTER) {
+      // raster rows of this block's segments (scalar: the same in every lane),
+      // one scalar base per tensor and a 32-bit lane offset per segment
+      uint32_t offs[Cp::PT];
+#pragma unroll
+      for (int e = 0; e < Cp::PT; ++e)
+        offs[e] = __builtin_amdgcn_readfirstlane(seg_intra[jb * (KB / Cp::RPS) + copier.wave_u + e * NW]);
+      next_block();
+      copier.issue_rows_origin(kb, vb, org, offs, kl, vl);
     } else {
-      copier.issue(kb, vb, (size_t)next_key0(), kl, vl);
+      const size_t row0 = (size_t)org + (size_t)(jb * KB);
+      next_block();
+      if constexpr (MASS)
+        copier.issue_k(kb, row0, kl);
+      else
+        copier.issue(kb, vb, row0, kl, vl);
     }
   };
 
-  // Padding masks (PADM, one instance each): 0 whole-tile latent, no mask;
-  // 1 tiles 8 keys wide with at most 64 tile rows; 2 any other tile.  Keys at
-  // padding positions of a partial key tile are masked out of the stage being
-  // computed, found by a second walk over the key blocks (in step with the
-  // stages, a few scalar instructions each, which the matrix products hide).
-  // PADM 1: a 32-key block is 4 tile rows of 8, and element e of lane l in
-  // the S^T accumulator holds row e / 4 of the block and column 4 (l / 32) +
-  // e % 4 of the tile.  A key is real when its row (i0, i1) and its column
-  // are: one bit per tile row (a ballot) and the tile's real width are worked
-  // out once per key tile, and a stage sets the scores of padding rows and
-  // columns to -inf (a select, so any finite padding contents, even ones whose
-  // products overflow, are masked exactly).
-  // PADM 2 tests every key of the block (ballot per stage).
-  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0, ckbt = tile_blocks(s0, s1);
-  bool key_tile_partial = false, col_partial = false;
-  uint64_t rows_real = ~0ull;  // bit R: tile row R is real
-  int col_ext = 8;             // real columns of the key tile
-  auto mask_keys = [&](f32x16 (&sacc)[QT]) {
+  // Padding mask: element e of lane l in the S^T accumulator holds key
+  // 8 (e / 4) + 4 (l / 32) + e % 4 of the block, so with compacted keys a
+  // stage whose block ends a partial tile sets the scores of keys at or past
+  // its real count to -inf (a select, so whatever the staged padding row
+  // holds is masked exactly).
+  auto mask_keys = [&](f32x16 (&sacc)[QT], const BlockInfo& bi) {
     if constexpr (PADM != 0) {
-      const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
-      if constexpr (PADM == 1) {
-        if (cjb == 0) {  // a new key tile
-          key_tile_partial = tile_partial(k0, k1, k2, g);
-          if (key_tile_partial) {
-            const int e0 = tile_ext(k0, g.t, g.T), e1 = tile_ext(k1, g.h, g.H), e2 = tile_ext(k2, g.w, g.W);
-            const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
-            const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
-            rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
-            col_ext = e2;
-            col_partial = e2 < 8;
-          }
-        }
-        if (key_tile_partial) {
-          const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
-          if (rb != 0xfu) {  // a row of the block is padding (uniform)
+      if (bi.nvalid != 0u) {  // uniform
+        // 4 (l / 32) worked out here, not held in a register across the loop
+        uint32_t l = (uint32_t)lane;
+        asm volatile("" : "+v"(l));
+        const int nv = (int)bi.nvalid - (int)((l >> 5) << 2);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const bool rreal = (rb >> u) & 1u;
+        for (int e = 0; e < 16; ++e) {
+          const bool real = 8 * (e >> 2) + (e & 3) < nv;
 #pragma unroll
-              for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                  sacc[qt][4 * u + jj] = rreal ? sacc[qt][4 * u + jj] : -INFINITY;
-            }
-          }
-          if (col_partial) {
-            bool creal[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) sacc[qt][e] = creal[e & 3] ? sacc[qt][e] : -INFINITY;
-          }
-        }
-      } else if (tile_partial(k0, k1, k2, g)) {
-        const uint32_t m = block_real_mask(k0, k1, k2, cjb * KB, g, lane);
-        if (m != 0xffffffffu) {  // blocks of a partial tile are often whole
-          const uint32_t bits = lane_bits(m, lane);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (!elem_real(bits, e)) sacc[qt][e] = -INFINITY;
-        }
-      }
-      if (++cjb == ckbt) {
-        cjb = 0;
-        if (++ci2 == w2) {
-          ci2 = 0;
-          if (++ci1 == w1) {
-            ci1 = 0;
-            ++ci0;
-          }
-          ckbt = tile_blocks(s0 + ci0, s1 + ci1);
+          for (int qt = 0; qt < QT; ++qt) sacc[qt][e] = real ? sacc[qt][e] : -INFINITY;
         }
       }
     }
@@ -597,7 +538,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
                    BlockInfo& bi_far) {
     f32x16 sacc[QT];
     qk_stage<D, QT>(kf, qf, sacc);
-    mask_keys(sacc);
+    mask_keys(sacc, bi_cur);
     if constexpr (MASS) {
       const bool tile_done = (bi_cur.mass >> 31) != 0u;
       const uint32_t member = bi_cur.mass & 0xffu;
@@ -738,20 +679,13 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   const int bpt = g.L / C::ROWS;
   const int total = B * Hh * g.ntiles * bpt;
   const int group = xcd_group_items(B * Hh, g.ntiles * bpt);
-  // Padded latents get instances of their own (the key mask, the zeroed or
-  // skipped padding rows).
-  {
-    if (g.padded) {
-      if (g.w == 8 && g.t * g.h <= 64)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 1>), dim3((uint32_t)total),
-                           dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh,
-                           scale * kLog2e, bpt, total, group);
-      else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 2>), dim3((uint32_t)total),
-                           dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh,
-                           scale * kLog2e, bpt, total, group);
-      return hipGetLastError();
-    }
+  // Padded latents get an instance of their own (compacted keys of partial
+  // tiles, the key mask, the zeroed or skipped padding rows).
+  if (g.padded) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 1>), dim3((uint32_t)total),
+                       dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh, scale * kLog2e,
+                       bpt, total, group);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NW, OCC, MASS, RASTER, 0>), dim3((uint32_t)total),
                      dim3(C::THREADS), 0, st, q, k, v, o, lse, g, ht, ma, B, Hh, scale * kLog2e,
@@ -761,7 +695,11 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
 
 }  // namespace
 
-bool fwd_bf16_supported(int D, int L) { return (D == 64 || D == 128) && L % 32 == 0; }
+// A padded latent's compacted key index (below L) is split with fp32
+// reciprocals, exact for indices below 2^21.
+bool fwd_bf16_supported(int D, const Geometry& g) {
+  return (D == 64 || D == 128) && g.L % 32 == 0 && (!g.padded || g.L <= (1 << 20));
+}
 
 template <bool RASTER>
 hipError_t launch_fwd_order(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
@@ -794,9 +732,7 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 bool fwd_raster_supported(int D, const Geometry& g) {
   // a copy segment (1 KiB) holds 1024 / (2 D) rows; they must be consecutive
   // raster rows, so the tile width must be a multiple of that count
-  // (padded latents: the copies' coordinate table packs t, h, w in 10 bits)
-  return fwd_bf16_supported(D, g.L) && g.w % (512 / D) == 0 && g.L / (512 / D) <= kMaxRasterSegs &&
-         (!g.padded || (g.t <= 1024 && g.h <= 1024 && g.w <= 1024));
+  return fwd_bf16_supported(D, g) && g.w % (512 / D) == 0 && g.L / (512 / D) <= kMaxRasterSegs;
 }
 
 hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -23,14 +23,15 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           float* dl, const Geometry& g, const HeadTable& ht, int B, int Hh, int D,
                           float scale, hipStream_t stream);
 
-// bf16 MFMA instance (D in {64, 128}, L % 32 == 0).
-bool fwd_bf16_supported(int D, int L);
+// bf16 MFMA instance (D in {64, 128}, L % 32 == 0, and L <= 2^20 for a
+// padded latent).
+bool fwd_bf16_supported(int D, const Geometry& g);
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            float* lse, const Geometry& g, const HeadTable& ht, int B, int Hh,
                            int D, float scale, hipStream_t stream);
 // The same forward on raster-order q, k, v, o and lse (the reorder folded into
-// the kernel's loads and stores): whole-tile latents whose tile width is a
-// multiple of 512 / D rows.
+// the kernel's loads and stores): latents whose tile width is a multiple of
+// 512 / D rows.
 bool fwd_raster_supported(int D, const Geometry& g);
 hipError_t launch_fwd_bf16_raster(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   uint16_t* o, float* lse, const Geometry& g, const HeadTable& ht,

@@ -185,23 +185,27 @@ struct KvDma {
       dma16(vbase + off, vl + seg * 1024);
     }
   }
-  // The same for a key tile that holds padding (a latent that is not a whole
-  // number of tiles): lanes whose row is padding (real[e] false) copy 16
-  // bytes of the origin row itself, a real row, so every staged value is
-  // finite and no read leaves the tensor; the attention masks those keys.
-  __device__ __forceinline__ void issue_rows_masked(const uint16_t* kg, const uint16_t* vg,
-                                                    uint32_t origin_row, const uint32_t (&seg_off)[PT],
-                                                    const bool (&real)[PT], int lane, char* kl,
-                                                    char* vl) const {
-    constexpr int CPR = D / 8;  // chunks per row
+  // Row of the block that the lane's copy of segment e fills (worked out at
+  // each use, like lane_off, rather than held in a register).
+  __device__ __forceinline__ uint32_t row_in_block(int e, int lane) const {
+    uint32_t l = (uint32_t)lane;
+    asm volatile("" : "+v"(l));
+    return (uint32_t)((wave_u + e * NW) * RPS) + l / (uint32_t)(D / 8);
+  }
+  // The same block gathered row by row (a key tile that holds padding, its
+  // real keys compacted): the lane's row of segment e is row_off[e] rows past
+  // origin_row (scalar).  Lanes whose row is padding (real[e] false) copy 16
+  // bytes of the origin row itself, a real row, so no read leaves the tensor;
+  // the attention masks those keys.
+  __device__ __forceinline__ void issue_rows_gather(const uint16_t* kg, const uint16_t* vg,
+                                                    uint32_t origin_row, const uint32_t (&row_off)[PT],
+                                                    const bool (&real)[PT], char* kl, char* vl) const {
     const char* kbase = (const char*)(kg + (size_t)origin_row * D);
     const char* vbase = (const char*)(vg + (size_t)origin_row * D);
-    const uint32_t pad_off = (uint32_t)(lane % CPR) * 16u;
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
       const int seg = wave_u + e * NW;
-      const uint32_t in_seg = goff[e] - (uint32_t)(seg * RPS * D * 2);
-      const uint32_t off = real[e] ? seg_off[e] * (uint32_t)(D * 2) + in_seg : pad_off;
+      const uint32_t off = (real[e] ? row_off[e] * (uint32_t)(D * 2) : 0u) + in_row(e);
       dma16(kbase + off, kl + seg * 1024);
       dma16(vbase + off, vl + seg * 1024);
     }
@@ -211,6 +215,19 @@ struct KvDma {
     const char* kbase = (const char*)(kg + row0 * D);
 #pragma unroll
     for (int e = 0; e < PT; ++e) dma16(kbase + lane_off(e), kl + (wave_u + e * NW) * 1024);
+  }
+  // The K block alone, gathered row by row as in issue_rows_gather.
+  __device__ __forceinline__ void issue_k_gather(const uint16_t* kg, uint32_t origin_row,
+                                                 const uint32_t (&row_off)[PT], const bool (&real)[PT],
+                                                 char* kl) const {
+    const char* kbase = (const char*)(kg + (size_t)origin_row * D);
+#pragma unroll
+    for (int e = 0; e < PT; ++e)
+      dma16(kbase + (real[e] ? row_off[e] * (uint32_t)(D * 2) : 0u) + in_row(e), kl + (wave_u + e * NW) * 1024);
+  }
+  // The lane's (swizzled) 16-byte chunk inside its row of segment e.
+  __device__ __forceinline__ uint32_t in_row(int e) const {
+    return lane_off(e) % (uint32_t)(D * 2);
   }
 };
 

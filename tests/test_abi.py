@@ -93,6 +93,8 @@ def test_forward_argument_errors(lib):
     assert fwd(lib, D=96, dt=L.STA_F32) == UNSUP
     assert fwd(lib, dt=7) == UNSUP
     assert fwd(lib, tile=(1, 4, 4), latent=(6, 16, 16)) == UNSUP   # L = 16 is not a multiple of 32
+    # a padded latent's compacted key index is split in fp32: L <= 2^20 (here 1024 * 1032)
+    assert fwd(lib, tile=(1, 1024, 1032), latent=(1, 1025, 1025)) == UNSUP
     assert fwd(lib, q=MIS) == ALIGN
     assert fwd(lib, lse=MIS) == ALIGN
     many = [(3, 3, 3)] * 257
@@ -107,9 +109,6 @@ def test_forward_raster_argument_errors(lib):
         return lib.sta_forward_raster(q, P, P, P, lse, 1, 2, D, d3(*latent), d3(*tile),
                                       w.ctypes.data_as(ctypes.c_void_p), 0.1, dt, NUL)
     assert fr(q=NUL) == ARG
-    # padded latents are taken (masked), but the copy table packs tile dims in 10 bits
-    assert lib.sta_forward_raster(P, P, P, P, NUL, 1, 2, 128, d3(1, 1, 3000), d3(1, 1, 2048),
-                                  w.ctypes.data_as(ctypes.c_void_p), 0.1, 0, NUL) == UNSUP
     assert fr(dt=L.STA_F32) == UNSUP
     assert fr(tile=(2, 8, 2), latent=(6, 16, 32)) == UNSUP    # copy segments of 4 rows span x-runs
     assert fr(D=64, tile=(2, 8, 4)) == UNSUP                   # D = 64: 8-row segments, width 4 too narrow
