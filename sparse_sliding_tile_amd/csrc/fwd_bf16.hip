@@ -193,6 +193,20 @@ __device__ __forceinline__ uint32_t raster_row(int a0, int a1, int a2, uint32_t 
          ((uint32_t)(a1 * g.h) + i1) * (uint32_t)g.W + (uint32_t)(a2 * g.w) + i2;
 }
 
+// Position (t, h, w) inside a partial tile of index c in its compacted order
+// (the tile's real tokens in (t, h, w) order, padding positions left out),
+// e1 and e2 the tile's real extents along h and w and inv1, inv2 their fp32
+// reciprocals.  Exact for c < 2^20: (c + 0.5) / e then lies at least 2^-21
+// (relative) away from any integer, beyond the reciprocal's error.
+struct TilePos {
+  uint32_t t, h, w;
+};
+__device__ __forceinline__ TilePos split_compact(uint32_t c, int e1, int e2, float inv1, float inv2) {
+  const uint32_t tr = (uint32_t)(((float)c + 0.5f) * inv2);  // tile row (t, h)
+  const uint32_t ct = (uint32_t)(((float)tr + 0.5f) * inv1);
+  return {ct, tr - ct * (uint32_t)e1, c - tr * (uint32_t)e2};
+}
+
 // MASS: the window mass (v and o unused): K blocks only, no P V; the head
 // table holds the full window and ma the candidate windows (see MassArgs).
 // RASTER: q, k, v, o and lse are in raster order (a latent whose tile width
@@ -259,26 +273,40 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // Q^T fragments (B operand): lane holds 8 consecutive d of its query row.
   // qrow[qt]: the lane's query row inside the sequence (tile-major, or its
   // raster position).
-  // A raster-order tensor has no rows for padding positions: their queries
-  // are zeros here and their outputs are not written.
+  // Padded latents: the real query rows of a partial tile are taken
+  // compacted, as the keys below: workgroup sub of the tile takes compacted
+  // rows [sub * ROWS, (sub + 1) * ROWS), so the tile needs ceil(real / ROWS)
+  // workgroups and the rest find no real row.  A lane past the real count
+  // has no query: it loads zeros and writes nothing for it.
   const int qrow0 = qtile * g.L + sub * C::ROWS + wave * QT * 32;
+  int qn = g.L;  // real query rows of the tile
+  int qe1 = g.h, qe2 = g.w;
+  if constexpr (PADM != 0) {
+    qe1 = tile_ext(a1, g.h, g.H);
+    qe2 = tile_ext(a2, g.w, g.W);
+    qn = tile_ext(a0, g.t, g.T) * qe1 * qe2;
+  }
   uint32_t qrow[QT];
   bool qreal[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int tm = qrow0 + qt * 32 + c32;
-    qreal[qt] = PADM == 0 || token_real(a0, a1, a2, tm - qtile * g.L, g);
-    qrow[qt] = RASTER ? (qreal[qt] ? raster_row(a0, a1, a2, (uint32_t)(tm - qtile * g.L), g) : 0u)
-                      : (uint32_t)tm;
+    const int ci = qrow0 - qtile * g.L + qt * 32 + c32;  // row inside the tile (compacted if padded)
+    uint32_t r = (uint32_t)ci;
+    qreal[qt] = PADM == 0 || ci < qn;
+    if (PADM != 0 && qn < g.L) {
+      const TilePos tp = split_compact((uint32_t)ci, qe1, qe2, __builtin_amdgcn_rcpf((float)qe1),
+                                       __builtin_amdgcn_rcpf((float)qe2));
+      r = (tp.t * (uint32_t)g.h + tp.h) * (uint32_t)g.w + tp.w;
+    }
+    qrow[qt] = !qreal[qt] ? 0u : RASTER ? raster_row(a0, a1, a2, r, g) : (uint32_t)(qtile * g.L) + r;
   }
   bf16x8 qf[QT][C::KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      qf[qt][ks] = (!RASTER || qreal[qt])
-                       ? as_bf16x8(*(const u32x4*)(q + (seq + qrow[qt]) * D + ks * 16 + grp * 8))
-                       : bf16x8{};
+      qf[qt][ks] = qreal[qt] ? as_bf16x8(*(const u32x4*)(q + (seq + qrow[qt]) * D + ks * 16 + grp * 8))
+                             : bf16x8{};
   const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
   const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
             s2 = window_start(a2, w2, g.n2);
@@ -303,6 +331,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       const int cnt = (c0 ? l0 : w0 - l0) * (c1 ? l1 : w1 - l1) * (c2 ? l2 : w2 - l2);
       nblk += cnt * tile_blocks(c0 ? x0 : g.t, c1 ? x1 : g.h, c2 ? x2 : g.w);
     }
+    if (sub * C::ROWS >= qn) nblk = 0;  // no real query row here: straight to the epilogue
   }
 
   // Mass instance: the start of every candidate window of this query tile
@@ -405,10 +434,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     uint32_t mass;
   };
   // A partial key tile's block: the lane's key of each of its copy segments
-  // is compacted key c = jb * 32 + row, at (c / (e1 e2), (c / e2) % e1,
-  // c % e2) inside the tile (e = the real extents).  The quotients are taken
-  // in fp32 with the reciprocal: c < 2^20, so (c + 0.5) / e lies at least
-  // 2^-21 (relative) away from any integer, beyond the reciprocal's error.
+  // is compacted key c = jb * 32 + row of the tile.
   auto issue = [&](char* kl, char* vl, BlockInfo& bi) __attribute__((always_inline)) {
     if constexpr (PADM != 0) bi.nvalid = jb == kbt - 1 ? (uint32_t)(knreal - jb * KB) & (KB - 1) : 0u;
     if constexpr (MASS) bi.mass = kmember | (jb == kbt - 1 ? 0x80000000u : 0u);
@@ -421,12 +447,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < Cp::PT; ++e) {
         const uint32_t c = (uint32_t)(jb * KB) + copier.row_in_block(e, lane);
-        const uint32_t tr = (uint32_t)(((float)c + 0.5f) * kinv2);  // tile row (t, h)
-        const uint32_t cw = c - tr * (uint32_t)ke2;
-        const uint32_t ct = (uint32_t)(((float)tr + 0.5f) * kinv1);
-        const uint32_t ch = tr - ct * (uint32_t)ke1;
+        const TilePos tp = split_compact(c, ke1, ke2, kinv1, kinv2);
         real[e] = c < (uint32_t)knreal;
-        rel[e] = ct * sa + ch * sb + cw;
+        rel[e] = tp.t * sa + tp.h * sb + tp.w;
       }
       next_block();
       if constexpr (MASS)
@@ -504,7 +527,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   constexpr int AHEAD = SLOTS == 4 ? 3 : 2;
   constexpr int PER = MASS ? KvDma<D, KB, NW>::PT : KvDma<D, KB, NW>::PER;
   BlockInfo bi0{}, bi1{}, bi2{}, bi3{};  // ring slots 0..3
-  issue(kl0, vl0, bi0);
+  if (nblk > 0) issue(kl0, vl0, bi0);
   if (nblk > 1) issue(kl1, vl1, bi1);
   if constexpr (SLOTS == 4) {
     if (nblk > 2) issue(kl2, vl2, bi2);
@@ -618,26 +641,43 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     }
   }
 
-  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; zero on padding rows.
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 on the lane's query row.
+  // Padded tile-major tensors: each lane also writes zeros (O and LSE) to
+  // the row at its uncompacted position when that position is padding, so
+  // every padding row of the tile is zeroed once and every real row is
+  // written once, by the lane that took it.
   // Mass instance: row mass l_c / l per candidate, summed over the wave's 32
   // rows into one partial per (candidate, sequence, 32-row block).
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float lt = xsum32(lrun[qt]);
-    const int rin = qrow0 - qtile * g.L + qt * 32 + c32;  // row inside the query tile
-    const bool real = PADM == 0 || token_real(a0, a1, a2, rin, g);
+    const bool real = qreal[qt];
     const float inv = real ? 1.0f / lt : 0.0f;
     const size_t row = seq + qrow[qt];
-    if (RASTER && !real) continue;  // no raster row for a padding position
+    if constexpr (PADM != 0 && !RASTER) {
+      const int pos = qrow0 - qtile * g.L + qt * 32 + c32;  // uncompacted position in the tile
+      if (!token_real(a0, a1, a2, pos, g)) {
+        const size_t prow = seq + (size_t)(qtile * g.L + pos);
+        if constexpr (!MASS) {
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(bf16x4*)(o + prow * D + dt * 32 + 8 * i + 4 * grp) = bf16x4{};
+        } else if (ma.lse_last != nullptr && grp == 0) {
+          ma.lse_last[prow] = 0.0f;
+        }
+        if (lse != nullptr && grp == 0) lse[prow] = 0.0f;
+      }
+    }
     if constexpr (!MASS) {
-      // padding rows: a select, not a product (their sums need not be finite)
+      if (!real) continue;  // no query row
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bf16x4 w;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = (__bf16)(real ? oacc[qt][dt][4 * i + j] * inv : 0.0f);
+          for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qt][dt][4 * i + j] * inv);
           *(bf16x4*)(o + row * D + dt * 32 + 8 * i + 4 * grp) = w;
         }
     } else {
@@ -648,17 +688,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       for (int c = 0; c < kMaxCandidates; ++c) {
         if (c < ma.ncand) {
           const float lcs = xsum32(lcand[qt][c]);
-          float r = real ? lcs * inv : 0.0f;  // a select: 0 on padding rows
+          float r = real ? lcs * inv : 0.0f;  // a select: 0 past the real rows
           // sum over the 32 rows (lanes 0..31; lanes 32..63 hold the same rows)
 #pragma unroll
           for (int off = 16; off > 0; off >>= 1) r += __shfl_xor(r, off, 32);
           if (lane == 0) ma.partial[((size_t)c * B * Hh + bh) * nblk32 + blk] = r;
-          if (c == ma.ncand - 1 && ma.lse_last != nullptr && grp == 0)
-            ma.lse_last[row] = real ? (mrun[qt] + log2f(lcs)) * kLn2 : 0.0f;
+          if (c == ma.ncand - 1 && ma.lse_last != nullptr && grp == 0 && real)
+            ma.lse_last[row] = (mrun[qt] + log2f(lcs)) * kLn2;
         }
       }
+      if (!real) continue;
     }
-    if (lse != nullptr && grp == 0) lse[row] = real ? (mrun[qt] + log2f(lt)) * kLn2 : 0.0f;
+    if (lse != nullptr && grp == 0) lse[row] = (mrun[qt] + log2f(lt)) * kLn2;
   }
 }
 

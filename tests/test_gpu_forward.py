@@ -154,13 +154,14 @@ def test_forward_raster_matches_oracle_and_reorder_path(sta, latent, tile, B, wi
 
 RASTER_PADDED_CASES = [  # latent, tile, B, windows, D: padded latents in one launch
     ((5, 15, 13), (2, 4, 4), 2, [(3, 3, 3), (2, 1, 4)], 128),    # -> (6, 16, 16), L = 32, one wave
-    # -> (12, 32, 32), L = 128, four waves; last-t tiles: 64 real keys in 2 of 4 key blocks, 2 query
-    # waves idle; the corner tile's 30 real keys (1 x 6 x 5) compacted into one masked block
+    # -> (12, 32, 32), L = 128, four waves; last-t tiles: 64 real keys in 2 of 4 key blocks and 64 real
+    # query rows in 2 of 4 waves (2 idle); the corner tile's 30 real tokens (1 x 6 x 5) compacted into
+    # one masked key block and one wave
     ((11, 30, 29), (2, 8, 8), 1, [(3, 3, 3), (1, 2, 2)], 128),
     ((3, 14, 29), (1, 8, 8), 1, [(1, 3, 3), (3, 1, 5)], 128),    # -> (3, 16, 32), L = 64, two waves
     ((5, 16, 20), (1, 8, 8), 1, [(3, 3, 3)], 64),                # D = 64 (8-row copy segments)
-    # L = 96, partial in every dim; the corner tile's 7 real keys (1 x 1 x 7) in one masked block, 2 query
-    # waves idle
+    # L = 96, one-wave workgroups, partial in every dim; the corner tile's 7 real tokens (1 x 1 x 7) in
+    # one masked key block and one workgroup (the tile's other two find no real row)
     ((7, 9, 23), (3, 4, 8), 1, [(3, 3, 3), (1, 2, 2)], 128),
 ]
 
