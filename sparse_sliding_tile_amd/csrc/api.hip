@@ -259,7 +259,7 @@ int sta_backward(const void* q, const void* k, const void* v, const void* o, con
     if (misaligned(p)) return STA_ERR_ALIGN;
   const hipStream_t s = (hipStream_t)stream;
   if (dt == STA_BF16) {
-    if (!bwd_bf16_supported((int)D, g.L)) return STA_ERR_UNSUPPORTED;
+    if (!bwd_bf16_supported((int)D, g)) return STA_ERR_UNSUPPORTED;
     return to_status(launch_bwd_bf16(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
         (const uint16_t*)dout, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, (float*)workspace,

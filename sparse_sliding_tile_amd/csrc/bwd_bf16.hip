@@ -173,8 +173,10 @@ __device__ __forceinline__ f32x16 contract_rows_from(const bf16x8 (&a)[D / 16], 
 // --------------------------------------------------------------------------
 // 2. dQ (query-major).  Workgroup = NW waves x 32 query rows of one tile.
 // --------------------------------------------------------------------------
-// PADM: 0 no padding; 1 padded latent with w = 8 and t*h <= 64 (row and column
-// mask); 2 any other padded latent (a ballot per partial stage).
+// PADM: 0 whole-tile latent; 1 padded latent: the real query rows and keys of
+// a partial tile are taken compacted, in the tile's (t, h, w) order with the
+// padding positions left out (as in the forward), so only a partial key
+// tile's last block can hold padding keys, at its end.
 template <int D, int NW, int OCC, int PADM>
 __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
     const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dq,
     Geometry g, HeadTable ht, int B, int Hh, float c_log2, float scale, int blocks_per_tile,
     int total, int group_items) {
-  constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2;
+  constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2, ROWS = NW * 32;
   // Two-slot K/V ring plus a per-wave tile holding the wave's dO rows (64 KB
   // per 4-wave workgroup, so two fit a CU at two waves per SIMD).
   __shared__ __attribute__((aligned(1024))) char kl0[TB];
@@ -204,9 +206,31 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   const size_t seq = ((size_t)b * Hh + head) * (size_t)g.S;
   const uint16_t* kb = k + seq * D;
   const uint16_t* vb = v + seq * D;
+  const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
 
-  const size_t row0 = seq + (size_t)qtile * g.L + sub * (NW * 32) + wave * 32;
-  const size_t row = row0 + c32;
+  // The workgroup's query rows: compacted rows [sub * ROWS, (sub + 1) * ROWS)
+  // of the tile; rows past its real count (padded latents) stand in with the
+  // tile's first row, a real token, and their dQ is not written.
+  int qn = g.L, qe1 = g.h, qe2 = g.w;
+  float qinv1 = 1.0f, qinv2 = 1.0f;
+  if constexpr (PADM != 0) {
+    qe1 = tile_ext(a1, g.h, g.H);
+    qe2 = tile_ext(a2, g.w, g.W);
+    qn = tile_ext(a0, g.t, g.T) * qe1 * qe2;
+    qinv1 = __builtin_amdgcn_rcpf((float)qe1);
+    qinv2 = __builtin_amdgcn_rcpf((float)qe2);
+  }
+  auto qrow_of = [&](int c) -> size_t {  // row inside the sequence of compacted row c
+    uint32_t r = (uint32_t)c;
+    if (PADM != 0 && qn < g.L) {
+      const TilePos tp = split_compact((uint32_t)c, qe1, qe2, qinv1, qinv2);
+      r = c < qn ? (tp.t * (uint32_t)g.h + tp.h) * (uint32_t)g.w + tp.w : 0u;
+    }
+    return (size_t)qtile * g.L + r;
+  };
+  const int cw0 = sub * ROWS + wave * 32;  // the wave's first compacted row
+  const bool qreal = PADM == 0 || cw0 + c32 < qn;
+  const size_t row = seq + qrow_of(cw0 + c32);
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(q + row * D + ks * 16 + grp * 8));
@@ -219,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
 #pragma unroll
     for (int seg = 0; seg < 32 / RPS; ++seg) {
       const int r = seg * RPS + rin;
-      dma16(dout + (row0 + r) * D + ((p ^ (int)swz<D>(r)) * 8), dotile + seg * 1024);
+      dma16(dout + (seq + qrow_of(cw0 + r)) * D + ((p ^ (int)swz<D>(r)) * 8), dotile + seg * 1024);
     }
   }
   const float lrow = lse2[row], ndrow = dl[row];  // -Dl
@@ -230,20 +254,76 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
 #pragma unroll
   for (int e = 0; e < 16; ++e) ndl16[e] = ndrow;
 
-  const int a2 = qtile % g.n2, a1 = (qtile / g.n2) % g.n1, a0 = qtile / (g.n2 * g.n1);
   const int w0 = ht.wp[head][0], w1 = ht.wp[head][1], w2 = ht.wp[head][2];
   const int s0 = window_start(a0, w0, g.n0), s1 = window_start(a1, w1, g.n1),
             s2 = window_start(a2, w2, g.n2);
   const int spt = g.L / kStage;
-  const int nst = w0 * w1 * w2 * spt;
-  int i0 = 0, i1 = 0, i2 = 0, jb = 0;
+  // Key blocks of the walk: L / 32 per whole key tile, ceil(real / 32) per
+  // partial one (compacted), summed over the 8 classes of tiles (last along
+  // t, h, w or not); none when the workgroup holds no real query row.
+  auto tile_blocks = [&](int e0, int e1, int e2) -> int { return (e0 * e1 * e2 + kStage - 1) / kStage; };
+  int nst = w0 * w1 * w2 * spt;
+  if constexpr (PADM != 0) {
+    const int x0 = tile_ext(g.n0 - 1, g.t, g.T), x1 = tile_ext(g.n1 - 1, g.h, g.H),
+              x2 = tile_ext(g.n2 - 1, g.w, g.W);
+    const int l0 = s0 + w0 == g.n0, l1 = s1 + w1 == g.n1, l2 = s2 + w2 == g.n2;
+    nst = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int c0 = c & 1, c1 = (c >> 1) & 1, c2 = c >> 2;
+      const int cnt = (c0 ? l0 : w0 - l0) * (c1 ? l1 : w1 - l1) * (c2 ? l2 : w2 - l2);
+      nst += cnt * tile_blocks(c0 ? x0 : g.t, c1 ? x1 : g.h, c2 ? x2 : g.w);
+    }
+    if (sub * ROWS >= qn) nst = 0;
+  }
+  using Cp = KvDma<D, kStage, NW>;
   // lane offsets of the K/V copies worked out once (scalar base per issue)
-  const KvDma<D, kStage, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
-  // first row of the walk's key tile, worked out when the walk enters it
-  int ktrow = ((s0 * g.n1 + s1) * g.n2 + s2) * g.L;
-  auto issue = [&](char* kl, char* vl) {
-    const int key0 = ktrow + jb * kStage;
-    if (++jb == spt) {
+  const Cp copier(__builtin_amdgcn_readfirstlane(wave), lane);
+  // The walk's key tile, worked out when the walk enters it: its first row
+  // and, with padding, its real extents, real key count and the reciprocals
+  // of its real extents along h and w.
+  int i0 = 0, i1 = 0, i2 = 0, jb = 0, kbt = spt;
+  uint32_t korg = 0;
+  int ke1 = g.h, ke2 = g.w, knreal = g.L;
+  bool kpart = false;
+  float kinv1 = 1.0f, kinv2 = 1.0f;
+  auto enter_tile = [&]() __attribute__((always_inline)) {
+    const int k0 = s0 + i0, k1 = s1 + i1, k2 = s2 + i2;
+    korg = (uint32_t)(((k0 * g.n1 + k1) * g.n2 + k2) * g.L);
+    if constexpr (PADM != 0) {
+      const int e0 = tile_ext(k0, g.t, g.T);
+      ke1 = tile_ext(k1, g.h, g.H);
+      ke2 = tile_ext(k2, g.w, g.W);
+      knreal = e0 * ke1 * ke2;
+      kpart = knreal < g.L;
+      kbt = tile_blocks(e0, ke1, ke2);
+      if (kpart) {
+        kinv1 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_amdgcn_rcpf((float)ke1))));
+        kinv2 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_amdgcn_rcpf((float)ke2))));
+      }
+    }
+  };
+  enter_tile();
+  // Copies the walk's next block into (kl, vl) and returns, for the stage
+  // that computes it, its real key count when it ends a partial key tile
+  // with padding (1..31), else 0.
+  auto issue = [&](char* kl, char* vl) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t nv = jb == kbt - 1 ? (uint32_t)(knreal - jb * kStage) & (kStage - 1) : 0u;
+    const uint32_t org = korg;
+    const bool gather = PADM != 0 && kpart;
+    uint32_t rel[Cp::PT];
+    bool real[Cp::PT];
+    if (gather) {
+#pragma unroll
+      for (int e = 0; e < Cp::PT; ++e) {
+        const uint32_t c = (uint32_t)(jb * kStage) + copier.row_in_block(e, lane);
+        const TilePos tp = split_compact(c, ke1, ke2, kinv1, kinv2);
+        real[e] = c < (uint32_t)knreal;
+        rel[e] = (tp.t * (uint32_t)g.h + tp.h) * (uint32_t)g.w + tp.w;
+      }
+    }
+    const size_t key0 = (size_t)org + (size_t)(jb * kStage);
+    if (++jb == kbt) {
       jb = 0;
       if (++i2 == w2) {
         i2 = 0;
@@ -252,82 +332,35 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
           ++i0;
         }
       }
-      ktrow = (((s0 + i0) * g.n1 + (s1 + i1)) * g.n2 + (s2 + i2)) * g.L;
+      enter_tile();
     }
-    copier.issue(kb, vb, (size_t)key0, kl, vl);
+    if (gather)
+      copier.issue_rows_gather(kb, vb, org, rel, real, kl, vl);
+    else
+      copier.issue(kb, vb, key0, kl, vl);
+    return nv;
   };
 
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  // Padded latents: keys at padding positions of a partial key tile get
-  // dS = 0 (a second walk over the key blocks, for the stage being computed).
-  // The S^T accumulator holds key 8i + 4(l/32) + jj of the stage in element
-  // 4i + jj: with w = 8 that is row 4 cjb + i of the tile and column
-  // 4(l/32) + jj, so one bit per tile row (a ballot) and the tile's real width,
-  // worked out once per key tile, mask a stage.  The mask is a select on dS
-  // itself, so padding keys whose scores or dP overflow (any finite contents)
-  // still give exactly zero.  PADM 2 tests every key of the block.
-  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
-  bool key_tile_partial = false, col_partial = false;
-  uint64_t rows_real = ~0ull;  // bit R: tile row R is real
-  int col_ext = 8;             // real columns of the key tile
-  auto mask_keys = [&](f32x16& x) {
-    if constexpr (PADM == 0) return;
-    const int k0 = s0 + ci0, k1 = s1 + ci1, k2 = s2 + ci2;
-    if constexpr (PADM == 1) {
-      if (cjb == 0) {  // a new key tile
-        key_tile_partial = tile_partial(k0, k1, k2, g);
-        if (key_tile_partial) {
-          const int e0 = tile_ext(k0, g.t, g.T), e1 = tile_ext(k1, g.h, g.H), e2 = tile_ext(k2, g.w, g.W);
-          const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
-          const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
-          rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
-          col_ext = e2;
-          col_partial = e2 < 8;
-        }
-      }
-      if (key_tile_partial) {
-        const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
-        if (rb != 0xfu) {  // a row of the block is padding (uniform)
+  // Padding keys: element 4i + jj of the S^T accumulator holds key
+  // 8i + 4(l/32) + jj of the stage, so a stage whose block ends a partial key
+  // tile sets dS of the keys at or past its real count nv to zero (a select,
+  // so whatever the staged padding row holds gives exactly zero).
+  auto mask_keys = [&](f32x16& x, uint32_t nv) {
+    if constexpr (PADM != 0) {
+      if (nv != 0u) {  // uniform
+        const int n = (int)nv - 4 * grp;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool rreal = (rb >> u) & 1u;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) x[4 * u + jj] = rreal ? x[4 * u + jj] : 0.0f;
-          }
-        }
-        if (col_partial) {
-          bool creal[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) x[e] = creal[e & 3] ? x[e] : 0.0f;
-        }
-      }
-    } else if (tile_partial(k0, k1, k2, g)) {
-      const uint32_t m = block_real_mask(k0, k1, k2, cjb * kStage, g, lane);
-      if (m != 0xffffffffu) {
-        const uint32_t bits = lane_bits(m, lane);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = elem_real(bits, e) ? x[e] : 0.0f;
-      }
-    }
-    if (++cjb == spt) {
-      cjb = 0;
-      if (++ci2 == w2) {
-        ci2 = 0;
-        if (++ci1 == w1) {
-          ci1 = 0;
-          ++ci0;
-        }
+        for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + (e & 3) < n ? x[e] : 0.0f;
       }
     }
   };
 
   bf16x8 dof[KS];  // the wave's dO rows (B operand of dP^T), read once from its tile
-  auto step = [&](const char* kl, const char* vl) {
+  auto step = [&](const char* kl, const char* vl, uint32_t nv) {
     bf16x8 kf[KS], vr[KS];
     read_rows<D>(kl, kf, grp, c32);
     read_rows<D>(vl, vr, grp, c32);
@@ -341,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
       const float p = __builtin_amdgcn_exp2f(fmaf(st[e], c_log2, -lrow));
       dsf[e] = p * dpt[e];
     }
-    mask_keys(dsf);
+    mask_keys(dsf, nv);
     bf16x8 ds[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -358,9 +391,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   // Two-stage LDS ring: stage j sits in slot j % 2; its copy is issued two
   // stages ahead, right after the barrier that ends stage j - 2 (every wave
   // has then finished reading that slot: each step consumes its reads).
-  constexpr int PER = KvDma<D, kStage, NW>::PER;  // copies per wave per stage
-  issue(kl0, vl0);
-  if (nst > 1) issue(kl1, vl1);
+  constexpr int PER = Cp::PER;  // copies per wave per stage
+  uint32_t nv0 = 0, nv1 = 0;    // the real-key count of each slot's block
+  if (nst > 0) nv0 = issue(kl0, vl0);
+  if (nst > 1) nv1 = issue(kl1, vl1);
   wait_stage<PER>(nst > 1 ? 1 : 0);   // the dO tile and stage 0 have landed
   read_rows<D>(dotile, dof, grp, c32);  // the wave's own tile: no barrier needed
   barrier_lds();
@@ -369,32 +403,43 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dq_kernel(
   // runs after it.
   int j = 0;
   for (; j + 1 < nst; j += 2) {
-    step(kl0, vl0);
+    step(kl0, vl0, nv0);
     wait_dma();
     barrier_lds();
-    if (j + 2 < nst) issue(kl0, vl0);
-    step(kl1, vl1);
+    if (j + 2 < nst) nv0 = issue(kl0, vl0);
+    step(kl1, vl1, nv1);
     if (j + 2 < nst) {
       wait_dma();
       barrier_lds();
-      if (j + 3 < nst) issue(kl1, vl1);
+      if (j + 3 < nst) nv1 = issue(kl1, vl1);
     }
   }
-  if (j < nst) step(kl0, vl0);
+  if (j < nst) step(kl0, vl0, nv0);
 
-  // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj; zero
-  // on padding rows.
-  const int rin = sub * (NW * 32) + wave * 32 + c32;  // row inside the query tile
-  const bool real = !g.padded || token_real(a0, a1, a2, rin, g);
+  // dQ = scale * dQ^T: lane holds query c32, d = dt*32 + 8i + 4g + jj.  With
+  // padding, a lane also writes zeros to the row at its uncompacted position
+  // when that position is padding, so every row of the tile is written once.
+  if constexpr (PADM != 0) {
+    const int pos = cw0 + c32;  // uncompacted position in the tile
+    if (!token_real(a0, a1, a2, pos, g)) {
+      const size_t prow = seq + (size_t)qtile * g.L + pos;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x4 w;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(real ? acc[dt][4 * i + jj] * scale : 0.0f);
-      *(bf16x4*)(dq + row * D + dt * 32 + 8 * i + 4 * grp) = w;
+        for (int i = 0; i < 4; ++i) *(bf16x4*)(dq + prow * D + dt * 32 + 8 * i + 4 * grp) = bf16x4{};
     }
+  }
+  if (qreal) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 w;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(acc[dt][4 * i + jj] * scale);
+        *(bf16x4*)(dq + row * D + dt * 32 + 8 * i + 4 * grp) = w;
+      }
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -411,10 +456,20 @@ __device__ __forceinline__ void dma_stats(const float* __restrict__ lse2, const 
   }
 }
 
+// The statistics of 32 arbitrary rows (a compacted block of a partial query
+// tile): lane l < 32 copies lse2 of row rows(l) to stat[4 l], lane 32 + l
+// copies dl of the same row to stat[128 + 4 l] (4-byte DMA, wave 0 only).
+__device__ __forceinline__ void dma_stats_gather(const float* __restrict__ lse2, const float* __restrict__ dl,
+                                                 size_t row, char* stat, int wave, int lane) {
+  if (wave == 0) __builtin_amdgcn_global_load_lds(lane < 32 ? lse2 + row : dl + row, (lds_ptr_t)stat, 4, 0, 0);
+}
+
 // MODE 0 computes dV (S = Q K^T, P, dV += P^T dO); MODE 1 computes dK
 // (S, dP = dO V^T, dS, dK += dS^T Q).  Two launches instead of one keep the
 // resident state of each under the register file (one fused kernel spills).
-// PADM as in the dQ pass, here for the query rows of partial query tiles.
+// PADM as in the dQ pass: with padding the workgroup's key rows and the
+// query blocks it walks are compacted, and only a partial query tile's last
+// block can hold padding queries, at its end.
 template <int D, int NW, int MODE, int OCC, int PADM>
 __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -422,7 +477,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
     const float* __restrict__ lse2, const float* __restrict__ dl, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, const int32_t* __restrict__ rank_tab, Geometry g, HeadTable ht,
     int B, int Hh, float c_log2, float scale, int blocks_per_tile) {
-  constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2;
+  constexpr int KS = D / 16, DT = D / 32, TB = kStage * D * 2, ROWS = NW * 32;
   __shared__ __attribute__((aligned(1024))) char ql0[TB];
   __shared__ __attribute__((aligned(1024))) char dol0[TB];
   __shared__ __attribute__((aligned(1024))) char ql1[TB];
@@ -441,15 +496,37 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   const size_t seq = ((size_t)b * Hh + head) * (size_t)g.S;
   const uint16_t* qb = q + seq * D;
   const uint16_t* db = dout + seq * D;
+  const int a2 = ktile % g.n2, a1 = (ktile / g.n2) % g.n1, a0 = ktile / (g.n2 * g.n1);
+
+  // The workgroup's key rows: compacted rows [sub * ROWS, (sub + 1) * ROWS)
+  // of the key tile; rows past its real count (padded latents) stand in with
+  // the tile's first row, a real token, and their dK, dV are not written.
+  int kn = g.L, ke1 = g.h, ke2 = g.w;
+  float kinv1 = 1.0f, kinv2 = 1.0f;
+  if constexpr (PADM != 0) {
+    ke1 = tile_ext(a1, g.h, g.H);
+    ke2 = tile_ext(a2, g.w, g.W);
+    kn = tile_ext(a0, g.t, g.T) * ke1 * ke2;
+    kinv1 = __builtin_amdgcn_rcpf((float)ke1);
+    kinv2 = __builtin_amdgcn_rcpf((float)ke2);
+  }
+  auto krow_of = [&](int c) -> size_t {  // row inside the sequence of compacted key row c
+    uint32_t r = (uint32_t)c;
+    if (PADM != 0 && kn < g.L) {
+      const TilePos tp = split_compact((uint32_t)c, ke1, ke2, kinv1, kinv2);
+      r = c < kn ? (tp.t * (uint32_t)g.h + tp.h) * (uint32_t)g.w + tp.w : 0u;
+    }
+    return (size_t)ktile * g.L + r;
+  };
+  const int cw0 = sub * ROWS + wave * 32;  // the wave's first compacted key row
 
   // Resident key rows: K^T as the B operand (lane holds 8 d of key c32); for
   // dK the wave's 32 V rows are copied into its LDS tile (swizzled like the
   // staged tiles) and read from there once into registers (vrow).
-  const size_t krow0 = seq + (size_t)ktile * g.L + sub * (NW * 32) + wave * 32;
+  const size_t krow = seq + krow_of(cw0 + c32);
   bf16x8 kf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    kf[ks] = as_bf16x8(*(const u32x4*)(k + (krow0 + c32) * D + ks * 16 + grp * 8));
+  for (int ks = 0; ks < KS; ++ks) kf[ks] = as_bf16x8(*(const u32x4*)(k + krow * D + ks * 16 + grp * 8));
   char* vtile = vres + (MODE == 1 ? wave * TB : 0);
   bf16x8 vrow[MODE == 1 ? KS : 1];
   if constexpr (MODE == 1) {
@@ -458,27 +535,87 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
 #pragma unroll
     for (int seg = 0; seg < 32 / RPS; ++seg) {
       const int r = seg * RPS + rin;
-      dma16(v + (krow0 + r) * D + ((p ^ (int)swz<D>(r)) * 8), vtile + seg * 1024);
+      dma16(v + (seq + krow_of(cw0 + r)) * D + ((p ^ (int)swz<D>(r)) * 8), vtile + seg * 1024);
     }
   }
 
   // Query tiles whose window holds this key tile: a box [lo, hi] per dimension.
-  const int a2 = ktile % g.n2, a1 = (ktile / g.n2) % g.n1, a0 = ktile / (g.n2 * g.n1);
   int lo0, hi0, lo1, hi1, lo2, hi2;
   window_transpose(a0, ht.wp[head][0], g.n0, &lo0, &hi0);
   window_transpose(a1, ht.wp[head][1], g.n1, &lo1, &hi1);
   window_transpose(a2, ht.wp[head][2], g.n2, &lo2, &hi2);
   const int c0 = hi0 - lo0 + 1, c1 = hi1 - lo1 + 1, c2 = hi2 - lo2 + 1;
   const int spt = g.L / kStage;
-  const int nst = c0 * c1 * c2 * spt;
-  int i0 = 0, i1 = 0, i2 = 0, jb = 0;
+  // Query blocks of the walk: L / 32 per whole query tile, ceil(real / 32)
+  // per partial one, summed over the 8 classes of tiles (last along t, h, w
+  // or not); none when the workgroup holds no real key row.
+  auto tile_blocks = [&](int e0, int e1, int e2) -> int { return (e0 * e1 * e2 + kStage - 1) / kStage; };
+  int nst = c0 * c1 * c2 * spt;
+  if constexpr (PADM != 0) {
+    const int x0 = tile_ext(g.n0 - 1, g.t, g.T), x1 = tile_ext(g.n1 - 1, g.h, g.H),
+              x2 = tile_ext(g.n2 - 1, g.w, g.W);
+    const int l0 = hi0 == g.n0 - 1, l1 = hi1 == g.n1 - 1, l2 = hi2 == g.n2 - 1;
+    nst = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int e0 = c & 1, e1 = (c >> 1) & 1, e2 = c >> 2;
+      const int cnt = (e0 ? l0 : c0 - l0) * (e1 ? l1 : c1 - l1) * (e2 ? l2 : c2 - l2);
+      nst += cnt * tile_blocks(e0 ? x0 : g.t, e1 ? x1 : g.h, e2 ? x2 : g.w);
+    }
+    if (sub * ROWS >= kn) nst = 0;
+  }
+  using Cp = KvDma<D, kStage, NW>;
   // lane offsets of the Q/dO copies worked out once (scalar base per issue)
-  const KvDma<D, kStage, NW> copier(__builtin_amdgcn_readfirstlane(wave), lane);
-  // first row of the walk's query tile, worked out when the walk enters it
-  int qtrow = ((lo0 * g.n1 + lo1) * g.n2 + lo2) * g.L;
-  auto issue = [&](char* ql, char* dol, char* st) {
-    const size_t q0 = (size_t)(qtrow + jb * kStage);
-    if (++jb == spt) {
+  const Cp copier(__builtin_amdgcn_readfirstlane(wave), lane);
+  // The walk's query tile, worked out when the walk enters it: its first row
+  // and, with padding, its real extents, real row count and the reciprocals
+  // of its real extents along h and w.
+  int i0 = 0, i1 = 0, i2 = 0, jb = 0, qbt = spt;
+  uint32_t qorg = 0;
+  int qe1 = g.h, qe2 = g.w, qnreal = g.L;
+  bool qpart = false;
+  float qinv1 = 1.0f, qinv2 = 1.0f;
+  auto enter_tile = [&]() __attribute__((always_inline)) {
+    const int t0 = lo0 + i0, t1 = lo1 + i1, t2 = lo2 + i2;
+    qorg = (uint32_t)(((t0 * g.n1 + t1) * g.n2 + t2) * g.L);
+    if constexpr (PADM != 0) {
+      const int e0 = tile_ext(t0, g.t, g.T);
+      qe1 = tile_ext(t1, g.h, g.H);
+      qe2 = tile_ext(t2, g.w, g.W);
+      qnreal = e0 * qe1 * qe2;
+      qpart = qnreal < g.L;
+      qbt = tile_blocks(e0, qe1, qe2);
+      if (qpart) {
+        qinv1 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_amdgcn_rcpf((float)qe1))));
+        qinv2 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_amdgcn_rcpf((float)qe2))));
+      }
+    }
+  };
+  enter_tile();
+  // Copies the walk's next query block (Q, dO and the rows' statistics) and
+  // returns, for the stage that computes it, its real row count when it ends
+  // a partial query tile with padding (1..31), else 0.
+  auto issue = [&](char* ql, char* dol, char* st) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t nv = jb == qbt - 1 ? (uint32_t)(qnreal - jb * kStage) & (kStage - 1) : 0u;
+    const uint32_t org = qorg;
+    const bool gather = PADM != 0 && qpart;
+    uint32_t rel[Cp::PT];
+    bool real[Cp::PT];
+    uint32_t srel = 0;  // the statistics row of this lane (lane % 32 of the block)
+    if (gather) {
+#pragma unroll
+      for (int e = 0; e < Cp::PT; ++e) {
+        const uint32_t c = (uint32_t)(jb * kStage) + copier.row_in_block(e, lane);
+        const TilePos tp = split_compact(c, qe1, qe2, qinv1, qinv2);
+        real[e] = c < (uint32_t)qnreal;
+        rel[e] = (tp.t * (uint32_t)g.h + tp.h) * (uint32_t)g.w + tp.w;
+      }
+      const uint32_t c = (uint32_t)(jb * kStage) + (uint32_t)c32;
+      const TilePos tp = split_compact(c, qe1, qe2, qinv1, qinv2);
+      srel = c < (uint32_t)qnreal ? (tp.t * (uint32_t)g.h + tp.h) * (uint32_t)g.w + tp.w : 0u;
+    }
+    const size_t q0 = (size_t)org + (size_t)(jb * kStage);
+    if (++jb == qbt) {
       jb = 0;
       if (++i2 == c2) {
         i2 = 0;
@@ -487,83 +624,38 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
           ++i0;
         }
       }
-      qtrow = (((lo0 + i0) * g.n1 + (lo1 + i1)) * g.n2 + (lo2 + i2)) * g.L;
+      enter_tile();
     }
-    copier.issue(qb, db, q0, ql, dol);
-    dma_stats<D>(lse2, dl, seq + q0, st, wave, lane);
+    if (gather) {
+      copier.issue_rows_gather(qb, db, org, rel, real, ql, dol);
+      dma_stats_gather(lse2, dl, seq + org + srel, st, wave, lane);
+    } else {
+      copier.issue(qb, db, q0, ql, dol);
+      dma_stats<D>(lse2, dl, seq + q0, st, wave, lane);
+    }
+    return nv;
   };
 
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  // Padded latents: the P (dV) or dS (dK) operand of padding query rows of a
-  // partial query tile is set to zero with a select, so any finite padding
-  // contents (even ones whose scores or dP overflow) contribute nothing.  A
-  // second walk over the query blocks follows the stage being computed.
-  // Element 4i + jj of the S accumulator holds query 8i + 4(l/32) + jj of the
-  // stage: with w = 8 that is row 4 cjb + i of the tile and column
-  // 4(l/32) + jj, so one bit per tile row (a ballot) and the tile's real width
-  // are worked out once per query tile (PADM 1); PADM 2 tests every query of
-  // the block.
-  int ci0 = 0, ci1 = 0, ci2 = 0, cjb = 0;
-  bool qtile_partial = false, col_partial = false;
-  uint64_t rows_real = ~0ull;  // bit R: tile row R is real
-  int col_ext = 8;             // real columns of the query tile
-  auto mask_queries = [&](float (&x)[16]) {
-    if constexpr (PADM == 0) return;
-    const int t0 = lo0 + ci0, t1 = lo1 + ci1, t2 = lo2 + ci2;
-    if constexpr (PADM == 1) {
-      if (cjb == 0) {  // a new query tile
-        qtile_partial = tile_partial(t0, t1, t2, g);
-        if (qtile_partial) {
-          const int e0 = tile_ext(t0, g.t, g.T), e1 = tile_ext(t1, g.h, g.H), e2 = tile_ext(t2, g.w, g.W);
-          const uint32_t r0 = fdiv((uint32_t)lane * 8u, g.fhw);  // lane / h (w = 8)
-          const uint32_t r1 = (uint32_t)lane - r0 * (uint32_t)g.h;
-          rows_real = __ballot(lane < g.t * g.h && (int)r0 < e0 && (int)r1 < e1);
-          col_ext = e2;
-          col_partial = e2 < 8;
-        }
-      }
-      if (qtile_partial) {
-        const uint32_t rb = (uint32_t)(rows_real >> (4 * cjb)) & 0xfu;
-        if (rb != 0xfu) {  // a row of the block is padding (uniform)
+  // Padding queries: element 4i + jj of the S accumulator holds query
+  // 8i + 4(l/32) + jj of the stage, so a stage whose block ends a partial
+  // query tile sets the P (dV) or dS (dK) operand of the queries at or past
+  // its real count nv to zero (a select, so whatever the staged padding row
+  // holds contributes exactly nothing).
+  auto mask_queries = [&](float (&x)[16], uint32_t nv) {
+    if constexpr (PADM != 0) {
+      if (nv != 0u) {  // uniform
+        const int n = (int)nv - 4 * grp;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool rreal = (rb >> u) & 1u;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) x[4 * u + jj] = rreal ? x[4 * u + jj] : 0.0f;
-          }
-        }
-        if (col_partial) {
-          bool creal[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) creal[jj] = 4 * grp + jj < col_ext;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) x[e] = creal[e & 3] ? x[e] : 0.0f;
-        }
-      }
-    } else if (tile_partial(t0, t1, t2, g)) {
-      const uint32_t m = block_real_mask(t0, t1, t2, cjb * kStage, g, lane);
-      if (m != 0xffffffffu) {
-        const uint32_t bits = lane_bits(m, lane);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = elem_real(bits, e) ? x[e] : 0.0f;
-      }
-    }
-    if (++cjb == spt) {
-      cjb = 0;
-      if (++ci2 == c2) {
-        ci2 = 0;
-        if (++ci1 == c1) {
-          ci1 = 0;
-          ++ci0;
-        }
+        for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + (e & 3) < n ? x[e] : 0.0f;
       }
     }
   };
 
-  auto step = [&](const char* ql, const char* dol, const char* st) {
+  auto step = [&](const char* ql, const char* dol, const char* st, uint32_t nv) {
     f32x16 s, dp;
     {
       bf16x8 qa[KS];
@@ -600,7 +692,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
         pe[e] = MODE == 0 ? p : p * dp[e];
       }
     }
-    mask_queries(pe);
+    mask_queries(pe, nv);
     // the second GEMM's operand reads start after the exponentials (measured
     // faster for dV than the compiler's interleave; dK is indifferent)
     __builtin_amdgcn_sched_barrier(0);
@@ -628,38 +720,46 @@ __global__ __launch_bounds__(64 * NW, OCC) void bwd_dkv_kernel(
   // The loop body holds both slots and has no exit in between (an exit
   // there made the compiler copy the accumulators every other stage); an
   // odd last stage runs after it.
-  issue(ql0, dol0, st0);
+  uint32_t nv0 = 0, nv1 = 0;  // the real-row count of each slot's block
+  if (nst > 0) nv0 = issue(ql0, dol0, st0);
   wait_dma();
   if constexpr (MODE == 1) read_rows<D>(vtile, vrow, grp, c32);  // the wave's own tile
   barrier_lds();
   int j = 0;
   for (; j + 1 < nst; j += 2) {
-    issue(ql1, dol1, st1);
-    step(ql0, dol0, st0);
+    nv1 = issue(ql1, dol1, st1);
+    step(ql0, dol0, st0, nv0);
     wait_dma();
     barrier_lds();
-    if (j + 2 < nst) issue(ql0, dol0, st0);
-    step(ql1, dol1, st1);
+    if (j + 2 < nst) nv0 = issue(ql0, dol0, st0);
+    step(ql1, dol1, st1, nv1);
     wait_dma();
     barrier_lds();
   }
-  if (j < nst) step(ql0, dol0, st0);
+  if (j < nst) step(ql0, dol0, st0, nv0);
 
-  // dK = scale * acc or dV = acc: lane holds key 8i + 4g + jj, d = dt*32 + c32;
-  // zero on padding rows.
+  // dK = scale * acc or dV = acc: lane holds key 8i + 4g + jj of the wave's
+  // 32, d = dt*32 + c32.  With padding, keys past the real count are not
+  // written, and each padding row of the tile gets zeros from the lane whose
+  // uncompacted position it is.
   uint16_t* out = MODE == 0 ? dv : dk;
   const float osc = MODE == 0 ? 1.0f : scale;
-  const uint32_t kbits =
-      g.padded ? lane_bits(block_real_mask(a0, a1, a2, sub * (NW * 32) + wave * 32, g, lane), lane)
-               : 0xffffffffu;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int e = 0; e < 16; ++e) {
+    const int kk = cw0 + 8 * (e >> 2) + 4 * grp + (e & 3);  // compacted (and uncompacted) index
+    if constexpr (PADM != 0) {
+      if (!token_real(a0, a1, a2, kk, g)) {
+        const size_t pr = seq + (size_t)ktile * g.L + kk;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const size_t r = krow0 + 8 * (e >> 2) + 4 * grp + (e & 3);
-      const __bf16 x = (__bf16)(elem_real(kbits, e) ? acc[dt][e] * osc : 0.0f);
-      out[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, x);
+        for (int dt = 0; dt < DT; ++dt) out[pr * D + dt * 32 + c32] = 0;
+      }
+      if (kk >= kn) continue;
     }
+    const size_t r = seq + krow_of(kk);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      out[r * D + dt * 32 + c32] = __builtin_bit_cast(uint16_t, (__bf16)(acc[dt][e] * osc));
+  }
 }
 
 inline int group_items_for(int seqs, int items_per_seq) {
@@ -693,8 +793,7 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                        st, q, k, v, dout, lse2, dl, dq, g, ht, B, Hh, c_log2, scale, bpt, total, group);
   };
   if (!g.padded) dq_pass(std::integral_constant<int, 0>{});
-  else if (g.w == 8 && g.t * g.h <= 64) dq_pass(std::integral_constant<int, 1>{});
-  else dq_pass(std::integral_constant<int, 2>{});
+  else dq_pass(std::integral_constant<int, 1>{});
   // dV asks for two waves per SIMD, except one-wave workgroups at D = 128,
   // whose registers allow one; dK fits two waves per SIMD in 4-wave
   // workgroups, smaller ones keep one.
@@ -708,14 +807,17 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                        c_log2, scale, bpt);
   };
   if (!g.padded) dkv_pass(std::integral_constant<int, 0>{});
-  else if (g.w == 8 && g.t * g.h <= 64) dkv_pass(std::integral_constant<int, 1>{});
-  else dkv_pass(std::integral_constant<int, 2>{});
+  else dkv_pass(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool bwd_bf16_supported(int D, int L) { return (D == 64 || D == 128) && L % 32 == 0; }
+// A padded latent's compacted row index (below L) is split with fp32
+// reciprocals, exact for indices below 2^21.
+bool bwd_bf16_supported(int D, const Geometry& g) {
+  return (D == 64 || D == 128) && g.L % 32 == 0 && (!g.padded || g.L <= (1 << 20));
+}
 
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const uint16_t* dout, const float* lse,

@@ -193,20 +193,6 @@ __device__ __forceinline__ uint32_t raster_row(int a0, int a1, int a2, uint32_t 
          ((uint32_t)(a1 * g.h) + i1) * (uint32_t)g.W + (uint32_t)(a2 * g.w) + i2;
 }
 
-// Position (t, h, w) inside a partial tile of index c in its compacted order
-// (the tile's real tokens in (t, h, w) order, padding positions left out),
-// e1 and e2 the tile's real extents along h and w and inv1, inv2 their fp32
-// reciprocals.  Exact for c < 2^20: (c + 0.5) / e then lies at least 2^-21
-// (relative) away from any integer, beyond the reciprocal's error.
-struct TilePos {
-  uint32_t t, h, w;
-};
-__device__ __forceinline__ TilePos split_compact(uint32_t c, int e1, int e2, float inv1, float inv2) {
-  const uint32_t tr = (uint32_t)(((float)c + 0.5f) * inv2);  // tile row (t, h)
-  const uint32_t ct = (uint32_t)(((float)tr + 0.5f) * inv1);
-  return {ct, tr - ct * (uint32_t)e1, c - tr * (uint32_t)e2};
-}
-
 // MASS: the window mass (v and o unused): K blocks only, no P V; the head
 // table holds the full window and ma the candidate windows (see MassArgs).
 // RASTER: q, k, v, o and lse are in raster order (a latent whose tile width

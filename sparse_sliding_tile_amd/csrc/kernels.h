@@ -55,7 +55,7 @@ hipError_t launch_mass_bf16(const uint16_t* q, const uint16_t* k, float* lse, co
 // mass[c][bh] = (sum of partial[c][bh][0 .. S/32)) / real rows.
 hipError_t launch_mass_reduce(const float* partial, float* mass, const Geometry& g, int ncand,
                               int64_t BH, hipStream_t stream);
-bool bwd_bf16_supported(int D, int L);
+bool bwd_bf16_supported(int D, const Geometry& g);
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const uint16_t* dout, const float* lse,
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dl,

@@ -113,6 +113,20 @@ __device__ __forceinline__ bool elem_real(uint32_t bits, int e) {
   return (bits >> (8 * (e >> 2) + (e & 3))) & 1u;
 }
 
+// Position (t, h, w) inside a partial tile of index c in its compacted order
+// (the tile's real tokens in (t, h, w) order, padding positions left out),
+// e1 and e2 the tile's real extents along h and w and inv1, inv2 their fp32
+// reciprocals.  Exact for c < 2^20: (c + 0.5) / e then lies at least 2^-21
+// (relative) away from any integer, beyond the reciprocal's error.
+struct TilePos {
+  uint32_t t, h, w;
+};
+__device__ __forceinline__ TilePos split_compact(uint32_t c, int e1, int e2, float inv1, float inv2) {
+  const uint32_t tr = (uint32_t)(((float)c + 0.5f) * inv2);  // tile row (t, h)
+  const uint32_t ct = (uint32_t)(((float)tr + 0.5f) * inv1);
+  return {ct, tr - ct * (uint32_t)e1, c - tr * (uint32_t)e2};
+}
+
 // x combined with the value of lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float xsum32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
