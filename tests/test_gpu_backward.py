@@ -60,8 +60,9 @@ def test_padding_contents_any_finite(sta, latent, tile, magnitude):
     with +-3e38, whose products overflow fp32 to +-inf (and their sums to
     NaN) inside the kernels.  Forward and backward outputs of real rows match
     the oracle on zero-padded inputs, and every output at a padding row is
-    exactly zero.  Covers both padding-mask modes (tile width 8 and 4) of the
-    forward, the dQ pass and the dK/dV pass."""
+    exactly zero.  Tile widths 8 and 4, partial tiles along every axis: the
+    kernels stage only real rows of partial tiles (compacted), so padding
+    contents must never reach a result."""
     wins = [(3, 3, 3), (2, 1, 3)]
     S = int(np.prod(latent))
     print(f"[padding contents] {latent} {tile} {magnitude}", flush=True)
