@@ -170,6 +170,9 @@ size_t sta_backward_workspace_bytes(int64_t B, int64_t Hh, int64_t D, sta_dim3 l
  *   dV_j = sum_i P_ij dO_i.
  * Inputs q, k, v, o, dout (tile-major, type dt) and lse (fp32, from
  * sta_forward); outputs dq, dk, dv (tile-major, type dt), fully overwritten.
+ * Sizes as sta_forward: STA_BF16 needs D in {64, 128}, L % 32 == 0 and, for a
+ * latent that is not a whole number of tiles, L <= 2^20 (STA_ERR_UNSUPPORTED
+ * otherwise).
  * workspace: device memory of at least sta_backward_workspace_bytes(), owned by
  * the caller, contents on entry irrelevant. */
 int sta_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,

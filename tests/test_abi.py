@@ -149,6 +149,10 @@ def test_backward_argument_errors(lib):
     assert bwd(dq=MIS) == ALIGN
     assert bwd(D=80) == UNSUP
     assert bwd(windows=NUL) == ARG
+    # a padded latent's compacted row index is split in fp32: L <= 2^20 (here 1024 * 1032)
+    big = (L.Dim3(1, 1025, 1025), L.Dim3(1, 1024, 1032))
+    nbig = lib.sta_backward_workspace_bytes(1, 2, 128, *big, 0)
+    assert lib.sta_backward(P, P, P, P, P, P, P, P, P, P, nbig, 1, 2, 128, *big, wp, 0.1, 0, NUL) == UNSUP
 
 
 def test_backward_noalloc_argument_errors(lib):
