@@ -116,7 +116,10 @@ class Timer:
 
 def source_hash(paths=None):
     """Hash of the forward kernel's code: its source and the headers it uses,
-    with comments and blank lines dropped (a comment edit is no kernel change)."""
+    with comments and blank lines dropped (a comment edit is no kernel change),
+    and the compiler flags of the build (without include paths, which differ
+    from machine to machine)."""
+    from sparse_sliding_tile_amd import build as libbuild
     h = hashlib.sha256()
     for path in paths or FWD_SOURCES:
         with open(path) as f:
@@ -124,6 +127,8 @@ def source_hash(paths=None):
                 code = line.split("//", 1)[0].rstrip()
                 if code:
                     h.update(code.encode() + b"\n")
+    fl = libbuild.FLAGS
+    h.update(" ".join(f for i, f in enumerate(fl) if f != "-I" and (i == 0 or fl[i - 1] != "-I")).encode())
     return h.hexdigest()[:16]
 
 
