@@ -350,6 +350,19 @@ def main():
         legs["tile_unreorder"] = {"ms": round(u_ms, 4), "GB/s": round(nbytes / u_ms / 1e6, 1),
                                   "frac_of_hbm_peak": round(nbytes / u_ms / 1e6 / PEAK_HBM_GBS, 3),
                                   "tensor": list(q.shape)}
+        # what a plain contiguous device copy of the same bytes reaches here
+        # (torch's copy_): the practical ceiling for the two copies above
+        ct = Timer(torch)
+        for _ in range(5):
+            with ct:
+                qt.copy_(q)
+        torch.cuda.synchronize()
+        c_ms = ct.total_ms() / 5
+        legs["plain_copy_reference"] = {
+            "ms": round(c_ms, 4), "GB/s": round(nbytes / c_ms / 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / c_ms / 1e6 / PEAK_HBM_GBS, 3),
+            "reorder_over_copy_rate": round(c_ms / r_ms, 3), "unreorder_over_copy_rate": round(c_ms / u_ms, 3),
+            "note": "torch's contiguous copy_ of the same tensor, same bytes read and written"}
         # (q, k, v, o, lse stay: the padded raster leg alternates with the bench step)
         del qt, kt, vt, ot
         torch.cuda.empty_cache()
