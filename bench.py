@@ -2,15 +2,16 @@
 """Benchmark of the Sliding Tile Attention hot path on one MI355X.
 
 One step = the whole forward path on one batch of the HunyuanVideo-shaped
-workload: tile reorder of Q, K, V (raster -> tile-major), sta_forward, tile
-unreorder of O, on latent (30, 48, 80), tile (6, 8, 8), 24 heads, head_dim 128,
-bf16, window (3, 3, 3) tiles for every head.  Inputs are seeded synthetic
-N(0, 1) tensors already resident in HBM when the timed region starts.
+workload: raster-order Q, K, V in, raster-order O and LSE out, in one launch of
+sta_forward_raster, whose loads do the tile reorder (raster -> tile-major) and
+whose stores the unreorder, on latent (30, 48, 80), tile (6, 8, 8), 24 heads,
+head_dim 128, bf16, window (3, 3, 3) tiles for every head.  Inputs are seeded
+synthetic N(0, 1) tensors already resident in HBM when the timed region starts.
 
 value = counted forward FLOPs per step / step time, where counted FLOPs are
 4 * L^2 * D per computed (query tile, key tile) pair (Q K^T and P V only; no
 skipped pair, no softmax).  The JSON line also carries:
-  roofline      the sta_forward kernel alone, timed with events on its stream;
+  roofline      the step's forward kernel, timed with events on its stream;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the workload;
   legs          the same step with separate reorder kernels; dense attention
                 from the same library (speedup denominator); reorder bandwidth;
