@@ -105,9 +105,12 @@ int sta_tile_unreorder(const void* y, void* x, int64_t B, int64_t Hh, int64_t D,
                        sta_dim3 tile, sta_dtype dt, void* stream);
 
 /* Number of (query tile, key tile) pairs over all heads: sum_h N_t * prod_d w'_d
- * ([STA-meth]: the blocks that are computed).  The transposed list has the same
- * count.  Host only; returns a negative STA_ERR_* code on bad arguments. */
-int64_t sta_tile_pairs_count(sta_dim3 latent, sta_dim3 tile, const int32_t* win_host, int64_t Hh);
+ * ([STA-meth]: the blocks that are computed), for the list sta_tile_pairs writes
+ * with the same transpose flag (0: query-major, 1: key-major; both orders hold
+ * the same pairs, so the count is the same).  Host only; returns a negative
+ * STA_ERR_* code on bad arguments (STA_ERR_ARG for a flag other than 0 or 1). */
+int64_t sta_tile_pairs_count(sta_dim3 latent, sta_dim3 tile, const int32_t* win_host, int64_t Hh,
+                             int transpose);
 
 /* Canonical tile-pair list, written by a kernel that uses the same window
  * function as sta_forward / sta_backward.  Tiles are numbered in raster order

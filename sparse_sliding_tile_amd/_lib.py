@@ -29,7 +29,7 @@ SIGNATURES = {
     "sta_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "sta_tile_reorder": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int, c_vp]),
     "sta_tile_unreorder": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, ctypes.c_int, c_vp]),
-    "sta_tile_pairs_count": (c_i64, [Dim3, Dim3, c_vp, c_i64]),
+    "sta_tile_pairs_count": (c_i64, [Dim3, Dim3, c_vp, c_i64, ctypes.c_int]),
     "sta_tile_pairs": (ctypes.c_int, [c_vp, c_vp, Dim3, Dim3, c_vp, c_i64, ctypes.c_int, c_vp]),
     "sta_tile_pairs_host": (ctypes.c_int, [c_vp, c_vp, Dim3, Dim3, c_vp, c_i64, ctypes.c_int]),
     "sta_forward": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, Dim3, Dim3, c_vp,
@@ -169,9 +169,10 @@ def tile_unreorder(y, latent, tile, out=None):
     return out
 
 
-def tile_pairs_count(latent, tile, windows):
+def tile_pairs_count(latent, tile, windows, transpose=False):
     w = _windows(windows, len(np.asarray(windows).reshape(-1, 3)))
-    n = lib().sta_tile_pairs_count(_dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), w.shape[0])
+    n = lib().sta_tile_pairs_count(_dim3(latent), _dim3(tile), w.ctypes.data_as(c_vp), w.shape[0],
+                                   1 if transpose else 0)
     if n < 0:
         raise StaError(int(n), "sta_tile_pairs_count")
     return int(n)
@@ -180,7 +181,7 @@ def tile_pairs_count(latent, tile, windows):
 def tile_pairs(latent, tile, windows, transpose=False, device="cuda"):
     """Pair list computed on the GPU: (int32 [P, 2] tensor, int64 offsets [Hh+1])."""
     w = _windows(windows, len(np.asarray(windows).reshape(-1, 3)))
-    n = tile_pairs_count(latent, tile, w)
+    n = tile_pairs_count(latent, tile, w, transpose)
     out = torch.empty((max(n, 1), 2), dtype=torch.int32, device=device)
     off = np.zeros(w.shape[0] + 1, dtype=np.int64)
     _check(lib().sta_tile_pairs(_dev(out, "pairs"), off.ctypes.data_as(c_vp), _dim3(latent), _dim3(tile),
@@ -192,7 +193,7 @@ def tile_pairs(latent, tile, windows, transpose=False, device="cuda"):
 def tile_pairs_host(latent, tile, windows, transpose=False):
     """Same list computed by the library on the host: (int32 [P, 2], int64 [Hh+1])."""
     w = _windows(windows, len(np.asarray(windows).reshape(-1, 3)))
-    n = tile_pairs_count(latent, tile, w)
+    n = tile_pairs_count(latent, tile, w, transpose)
     out = np.zeros((max(n, 1), 2), dtype=np.int32)
     off = np.zeros(w.shape[0] + 1, dtype=np.int64)
     _check(lib().sta_tile_pairs_host(out.ctypes.data_as(c_vp), off.ctypes.data_as(c_vp), _dim3(latent),

@@ -130,7 +130,9 @@ int sta_tile_unreorder(const void* y, void* x, int64_t B, int64_t Hh, int64_t D,
   return tile_copy(y, x, B, Hh, D, latent, tile, dt, stream, false);
 }
 
-int64_t sta_tile_pairs_count(sta_dim3 latent, sta_dim3 tile, const int32_t* win_host, int64_t Hh) {
+int64_t sta_tile_pairs_count(sta_dim3 latent, sta_dim3 tile, const int32_t* win_host, int64_t Hh,
+                             int transpose) {
+  if (transpose != 0 && transpose != 1) return STA_ERR_ARG;
   Geometry g;
   HeadTable ht;
   int st = make_geometry(latent, tile, &g);

@@ -235,9 +235,9 @@ def test_grid_dimension_limit(lib):
     more than 65535 tiles along a dimension is refused, never wrapped."""
     full = win([(1, 1, 65536)])
     fp = full.ctypes.data_as(ctypes.c_void_p)
-    assert lib.sta_tile_pairs_count(d3(1, 1, 65535 * 32), d3(1, 1, 32), fp, 1) == 65535 * 65535
-    assert lib.sta_tile_pairs_count(d3(1, 1, 65536 * 32), d3(1, 1, 32), fp, 1) == TOO_LARGE
-    assert lib.sta_tile_pairs_count(d3(65536, 1, 1), d3(1, 1, 1), fp, 1) == TOO_LARGE
+    assert lib.sta_tile_pairs_count(d3(1, 1, 65535 * 32), d3(1, 1, 32), fp, 1, 0) == 65535 * 65535
+    assert lib.sta_tile_pairs_count(d3(1, 1, 65536 * 32), d3(1, 1, 32), fp, 1, 0) == TOO_LARGE
+    assert lib.sta_tile_pairs_count(d3(65536, 1, 1), d3(1, 1, 1), fp, 1, 0) == TOO_LARGE
     # dense attention over 2^23 tokens picks 128-token tiles: 65536 of them
     assert lib.sta_dense_forward(P, P, P, P, NUL, 1, 2, 1 << 23, 128, 0.1, 0, NUL) == TOO_LARGE
     assert fwd(lib, latent=(1, 1, 65536 * 32), tile=(1, 1, 32), windows=((1, 1, 3), (1, 1, 3))) == TOO_LARGE
@@ -246,11 +246,16 @@ def test_grid_dimension_limit(lib):
 def test_pairs_argument_errors(lib):
     w = win([(3, 3, 3)])
     wp = w.ctypes.data_as(ctypes.c_void_p)
-    assert lib.sta_tile_pairs_count(d3(0, 16, 16), d3(4, 4, 4), wp, 1) == ARG
-    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), NUL, 1) == ARG
+    assert lib.sta_tile_pairs_count(d3(0, 16, 16), d3(4, 4, 4), wp, 1, 0) == ARG
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), NUL, 1, 0) == ARG
     bad = win([(0, 3, 3)])
-    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), bad.ctypes.data_as(ctypes.c_void_p), 1) == WINDOW
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), bad.ctypes.data_as(ctypes.c_void_p), 1, 0) == WINDOW
     assert lib.sta_tile_pairs(NUL, NUL, d3(6, 16, 16), d3(2, 4, 4), wp, 1, 0, NUL) == ARG
+    # the count takes the list's transpose flag: 0 or 1, the same count for both
+    n0 = lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), wp, 1, 0)
+    assert n0 == 48 * 27 and lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), wp, 1, 1) == n0
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), wp, 1, 2) == ARG
+    assert lib.sta_tile_pairs_count(d3(6, 16, 16), d3(2, 4, 4), wp, 1, -1) == ARG
 
 
 PAIR_CASES = [((6, 16, 16), (2, 4, 4), [(3, 3, 3), (1, 2, 5)]),
@@ -268,6 +273,7 @@ PAIR_CASES = [((6, 16, 16), (2, 4, 4), [(3, 3, 3), (1, 2, 5)]),
 def test_pair_count_matches_oracle(latent, tile, wins):
     _, off = O.tile_pairs(O.padded_latent(latent, tile), tile, wins)
     assert L.tile_pairs_count(latent, tile, wins) == off[-1]
+    assert L.tile_pairs_count(latent, tile, wins, transpose=True) == off[-1]
 
 
 @pytest.mark.parametrize("latent,tile,wins", PAIR_CASES)
